@@ -1,0 +1,313 @@
+"""Oracle: adaptive block-sparse self-attention for video DiTs, step by step.
+
+TEST INFRASTRUCTURE ONLY -- imported by tests/, the smoke check and the bench's
+CPU-baseline leg, never by the product path.  Everything is NumPy float64
+unless a step is defined on float32 scores; it shares no code with the HIP
+library.
+
+Sources (page title, section):
+  [FVA]  "FVAttn: Adaptive Sparse Attention with Runtime Load Balancing for
+         Video Generation" (full paper text, translated):
+         S2.1 block mask M_{h,i,j} from scores s_{h,i,j}; Top-p keeps the
+              smallest set of key blocks whose cumulative normalised importance
+              reaches p; a Top-k floor keeps a minimum budget per query block.
+         S2.2 Eq 1 per-head workload L_h = mean_i sum_j M_{h,i,j}; Eq 2 load
+              imbalance rho = max_r L_r / mean_r L_r.
+         S3.1 video-aware block reordering, block similarity from pooled Q/K,
+              the same routing pass yields per-head density and the
+              block-importance ordering.
+         S3.2 load balancing moves work, never changes the selected blocks.
+         S3.3 SASA adds not-yet-selected blocks in the routing's priority order
+              (no re-sort, no re-scoring).
+  [GSRS] "Sparse Attention for Video Generation Acceleration via Growing
+         Sparsity and Reduced Search":
+         S3.1/A.1 online softmax; S3.2 block-sparse FlashAttention skips
+         unselected key blocks; S5.3 block importance is normalised over the
+         key blocks of a query block (sums to 1); A.4 Top-p takes the shortest
+         descending prefix whose cumulative sum reaches p; A.6 token reordering
+         so that nearby space-time tokens share blocks.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * ordering: frame-major, spatial tiles tile_h x tile_w in raster order,
+    raster inside a tile, ragged edge tiles truncated; blocks are runs of B
+    consecutive positions (they may straddle tiles or frames);
+  * pooling: mean over the real tokens of a block (a short last block divides
+    by its own size);
+  * score: s_{h,i,j} = sm_scale * <qbar_{h,i}, kbar_{h,j}>, sm_scale = 1/sqrt(d);
+    importance = row softmax over j;
+  * ranking: scores compared as float32, descending, ties -> lower j first,
+    -0.0 == +0.0;
+  * cutoff arithmetic: importance weights are exp(s - s_max) in float64,
+    quantised to integers w = rint(e * 2^40) so that every cumulative sum is
+    exact; k_p = min{k : sum_{r<k} w_(r) >= fl(p * W)} with p taken as the
+    float32 value; p >= 1 keeps every block, p <= 0 keeps none before the floor;
+  * floor: k_i = max(k_p, min(k_min, nb)), per (head, query block) row;
+  * one-GPU SASA: every row gets e_i = min(nb - k_i, floor(k_i * refill / 1000))
+    more blocks, the next ones in the ranking;
+  * tile order: tiles sorted by kept count descending, then head, then query
+    block (longest-processing-time first).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+FIXED_POINT_BITS = 40
+
+
+# --------------------------------------------------------------------------
+# Geometry and the video-aware order  ([FVA] S3.1, [GSRS] A.6)
+# --------------------------------------------------------------------------
+
+def num_blocks(n_tokens: int, block: int) -> int:
+    return -(-n_tokens // block)
+
+
+def block_sizes(n_tokens: int, block: int) -> np.ndarray:
+    """r_b: number of real positions in block b (only the last may be short)."""
+    nb = num_blocks(n_tokens, block)
+    starts = np.arange(nb) * block
+    return np.minimum(block, n_tokens - starts).astype(np.int64)
+
+
+def token_order(grid: Tuple[int, int, int], tile: Tuple[int, int]) -> np.ndarray:
+    """pi: position -> natural token index, by explicit enumeration.
+
+    Frames in time order; inside a frame the spatial tiles in raster order
+    (tile rows top to bottom, tile columns left to right), edge tiles cut at the
+    frame border; inside a tile its tokens in raster order.  tile == (0, 0)
+    means no reordering.
+    """
+    T, H, W = grid
+    th, tw = tile
+    if th == 0 and tw == 0:
+        return np.arange(T * H * W, dtype=np.int64)
+    out = []
+    for t in range(T):
+        for a in range(-(-H // th)):
+            for c in range(-(-W // tw)):
+                for y in range(a * th, min(H, (a + 1) * th)):
+                    for x in range(c * tw, min(W, (c + 1) * tw)):
+                        out.append(t * H * W + y * W + x)
+    return np.asarray(out, dtype=np.int64)
+
+
+def padded_order(order: np.ndarray, block: int) -> np.ndarray:
+    """The order as nb*B slots, -1 in the slots past the end of the sequence."""
+    nb = num_blocks(len(order), block)
+    out = np.full(nb * block, -1, dtype=np.int64)
+    out[: len(order)] = order
+    return out
+
+
+# --------------------------------------------------------------------------
+# Pooled block representatives and block scores  ([FVA] S2.1, S3.1)
+# --------------------------------------------------------------------------
+
+def pool(x: np.ndarray, order: np.ndarray, block: int) -> np.ndarray:
+    """Mean of the rows of each block, in float64.  x: [H][N][d] -> [H][nb][d]."""
+    H, N, d = x.shape
+    nb = num_blocks(N, block)
+    out = np.zeros((H, nb, d))
+    for b in range(nb):
+        toks = order[b * block: min(N, (b + 1) * block)]
+        out[:, b, :] = x[:, toks, :].mean(axis=1)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, sm_scale: float) -> np.ndarray:
+    """s_{h,i,j} = sm_scale * <qbar_{h,i}, kbar_{h,j}>, float64 [H][nb][nb]."""
+    return sm_scale * np.einsum("hid,hjd->hij", qbar, kbar)
+
+
+def block_importance(scores: np.ndarray) -> np.ndarray:
+    """Normalised importance: softmax over key blocks j (each row sums to 1)."""
+    s = np.asarray(scores, dtype=np.float64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Ranking, Top-p with a Top-k floor  ([FVA] S2.1, S3.1; [GSRS] S5.2, A.4)
+# --------------------------------------------------------------------------
+
+def ranking(s_row: np.ndarray) -> np.ndarray:
+    """Key-block ids by float32 score descending, ties to the lower id."""
+    s = np.asarray(s_row, dtype=np.float32)
+    idx = np.arange(len(s))
+    return np.lexsort((idx, -s.astype(np.float64)))
+
+
+def fixed_point_weights(s_sorted: np.ndarray) -> np.ndarray:
+    """w_r = rint(exp(s_(r) - s_(0)) * 2^40) as exact integers (uint64)."""
+    s = np.asarray(s_sorted, dtype=np.float32).astype(np.float64)
+    e = np.exp(s - s[0])
+    return np.rint(e * float(2 ** FIXED_POINT_BITS)).astype(np.uint64)
+
+
+def topp_count(s_row: np.ndarray, top_p: float) -> int:
+    """k_p: length of the shortest ranked prefix whose cumulative weight reaches p."""
+    nb = len(s_row)
+    p = np.float32(top_p)
+    if p >= 1.0:
+        return nb
+    if p <= 0.0:
+        return 0
+    s_sorted = np.asarray(s_row, dtype=np.float32)[ranking(s_row)]
+    w = fixed_point_weights(s_sorted)
+    prefix = np.cumsum(w, dtype=np.uint64)  # exact: total < 2^51
+    target = float(p) * float(prefix[-1])
+    reached = np.flatnonzero(prefix.astype(np.float64) >= target)
+    return int(reached[0]) + 1 if len(reached) else nb
+
+
+def select_counts(scores32: np.ndarray, top_p: float, k_min: int):
+    """Per (head, query block) kept counts k_i and per-head totals.
+
+    scores32: float32 [H][nb][nb].  Returns (row_count int64 [H*nb],
+    head_count int64 [H]).
+    """
+    H, nqb, nkb = scores32.shape
+    floor = min(k_min, nkb)
+    rc = np.zeros(H * nqb, dtype=np.int64)
+    for h in range(H):
+        for i in range(nqb):
+            rc[h * nqb + i] = max(topp_count(scores32[h, i], top_p), floor)
+    return rc, rc.reshape(H, nqb).sum(axis=1)
+
+
+def kept_blocks(s_row: np.ndarray, count: int) -> np.ndarray:
+    """The first `count` ranked key blocks, as ascending ids."""
+    return np.sort(ranking(s_row)[:count])
+
+
+# --------------------------------------------------------------------------
+# Plan: one-GPU SASA refill, CSR mask, LPT tile order  ([FVA] S2.2, S3.2, S3.3)
+# --------------------------------------------------------------------------
+
+def refill_counts(row_count: np.ndarray, nb: int, refill_per_mille: int) -> np.ndarray:
+    rc = np.asarray(row_count, dtype=np.int64)
+    extra = np.minimum(nb - rc, (rc * int(refill_per_mille)) // 1000)
+    return rc + extra
+
+
+def plan(scores32: np.ndarray, row_count: np.ndarray, refill_per_mille: int) -> Dict[str, np.ndarray]:
+    H, nqb, nkb = scores32.shape
+    kept = refill_counts(row_count, nkb, refill_per_mille)
+    row_ptr = np.zeros(H * nqb + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(kept)
+    col_idx = np.zeros(int(row_ptr[-1]), dtype=np.int64)
+    for h in range(H):
+        for i in range(nqb):
+            r = h * nqb + i
+            col_idx[row_ptr[r]: row_ptr[r + 1]] = kept_blocks(scores32[h, i], int(kept[r]))
+    tiles = np.arange(H * nqb)
+    tile_order = np.array(sorted(tiles, key=lambda t: (-int(kept[t]), t // nqb, t % nqb)), dtype=np.int64)
+    return {
+        "kept": kept,
+        "row_ptr": row_ptr,
+        "col_idx": col_idx,
+        "head_count": kept.reshape(H, nqb).sum(axis=1),
+        "tile_order": tile_order,
+    }
+
+
+def head_workload(head_count: np.ndarray, nb: int) -> np.ndarray:
+    """Eq 1: L_h = mean over query blocks of the kept key-block count."""
+    return np.asarray(head_count, dtype=np.float64) / nb
+
+
+def imbalance(loads: Sequence[float]) -> float:
+    """Eq 2: rho = max load / mean load."""
+    x = np.asarray(loads, dtype=np.float64)
+    return float(x.max() / x.mean())
+
+
+# --------------------------------------------------------------------------
+# Attention  ([GSRS] S3.1, S3.2, A.1): exact softmax over the kept keys
+# --------------------------------------------------------------------------
+
+def _tile_tokens(order: np.ndarray, block: int, b: int) -> np.ndarray:
+    return order[b * block: min(len(order), (b + 1) * block)]
+
+
+def masked_attention(q, k, v, order, block, row_ptr, col_idx, sm_scale,
+                     tiles: Optional[Sequence[int]] = None):
+    """Softmax attention of every query over the keys of its row's kept blocks.
+
+    q, k, v: float64 [H][N][d] in natural token order.  Returns O [H][N][d] and
+    LSE [H][N] (natural log), NaN outside the requested tiles.
+    """
+    H, N, d = q.shape
+    nb = num_blocks(N, block)
+    o = np.full((H, N, d), np.nan)
+    lse = np.full((H, N), np.nan)
+    todo = range(H * nb) if tiles is None else tiles
+    for t in todo:
+        h, i = divmod(int(t), nb)
+        qt = _tile_tokens(order, block, i)
+        cols = col_idx[row_ptr[t]: row_ptr[t + 1]]
+        kt = np.concatenate([_tile_tokens(order, block, int(j)) for j in cols])
+        logits = sm_scale * (q[h, qt] @ k[h, kt].T)
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        l = p.sum(axis=1, keepdims=True)
+        o[h, qt] = (p @ v[h, kt]) / l
+        lse[h, qt] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def dense_attention(q, k, v, sm_scale, rows: Optional[np.ndarray] = None, chunk: int = 2048):
+    """Plain softmax attention over all N keys, float64; optionally a row subset."""
+    H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    o = np.zeros((H, len(rows), d))
+    lse = np.zeros((H, len(rows)))
+    for h in range(H):
+        for s in range(0, len(rows), chunk):
+            r = rows[s: s + chunk]
+            logits = sm_scale * (q[h, r] @ k[h].T)
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            l = p.sum(axis=1, keepdims=True)
+            o[h, s: s + len(r)] = (p @ v[h]) / l
+            lse[h, s: s + len(r)] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attention_recall(lse_kept: np.ndarray, lse_dense: np.ndarray) -> np.ndarray:
+    """Fraction of each query's full attention weight that falls on kept keys."""
+    return np.exp(lse_kept - lse_dense)
+
+
+def kept_flops(row_ptr, col_idx, n_tokens: int, block: int, head_dim: int) -> int:
+    """4 * d * sum over kept (i, j) of r_i * c_j (QK^T and PV multiply-adds)."""
+    r = block_sizes(n_tokens, block)
+    nb = len(r)
+    total = 0
+    for t in range(len(row_ptr) - 1):
+        i = t % nb
+        total += int(r[i]) * int(r[col_idx[row_ptr[t]: row_ptr[t + 1]]].sum())
+    return 4 * head_dim * total
+
+
+# --------------------------------------------------------------------------
+# The whole routing frontend on one GPU's heads
+# --------------------------------------------------------------------------
+
+def route(q, k, grid, tile, block, top_p, k_min, sm_scale=None):
+    """Order -> pool -> scores -> Top-p + floor.  q, k float64 [H][N][d]."""
+    H, N, d = q.shape
+    if sm_scale is None or sm_scale == 0:
+        sm_scale = 1.0 / math.sqrt(d)
+    order = token_order(grid, tile)
+    qbar = pool(q, order, block)
+    kbar = pool(k, order, block)
+    s64 = block_scores(qbar, kbar, sm_scale)
+    s32 = s64.astype(np.float32)
+    rc, hc = select_counts(s32, top_p, k_min)
+    return {"order": order, "qbar": qbar, "kbar": kbar, "scores64": s64, "scores32": s32,
+            "row_count": rc, "head_count": hc, "sm_scale": sm_scale}

@@ -1,0 +1,197 @@
+"""Seeded synthetic Q/K/V for per-head block-sparse video attention.
+
+Recipe (the same tensors feed the oracle and the HIP path):
+
+* Tokens live on a latent video grid (T frames x H rows x W columns) and are
+  numbered in natural raster order n = t*H*W + y*W + x.
+* A shared locality feature Phi[n] in R^d is a random Fourier feature map of
+  the grid coordinate (t, y, x): Phi[n, m] = sqrt(2/d) cos(w_m . x_n + b_m) with
+  w_m ~ N(0, sigma^-2 I_3) and b_m ~ U[0, 2 pi).  Its inner products
+  approximate a Gaussian bump exp(-|x - x'|^2 / (2 sigma^2)) in grid distance.
+* Per head h: Q_h = Xq_h + a_h Phi, K_h = Xk_h + a_h Phi, V_h = Xv_h, with
+  Xq, Xk, Xv ~ N(0, 1).  The locality amplitude a_h = sqrt(beta sqrt(d) / tau_h)
+  makes the locality part of a scaled logit q.k/sqrt(d) equal to
+  (beta / tau_h) times the bump, so tau_h acts as a per-head temperature:
+  small tau -> concentrated attention (few blocks kept), large tau or a_h = 0 ->
+  flat attention (many blocks kept).
+* Values are drawn in float64, rounded to float32 and then to bfloat16 with
+  round-to-nearest-even.  Tensors are returned as uint16 bf16 bit patterns,
+  layout [H][N][d] contiguous.
+
+Nothing here knows about blocks, scores, masks or softmax.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import functools
+from typing import Optional, Tuple
+
+import numpy as np
+
+# Locality strength constant (see module docstring).  Chosen once so that the
+# per-head block density of the 480p-style workload spans roughly an order of
+# magnitude for tau in [0.3, 3]; frozen here and reported by the bench.
+BETA = 96.0
+SIGMA = 2.0
+TAU_RANGE = (0.3, 3.0)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic attention problem (one GPU's share: heads x full sequence)."""
+
+    name: str
+    num_heads: int
+    head_dim: int
+    grid: Tuple[int, int, int]  # (T, H, W) latent grid
+    block: int  # q-block size == k-block size
+    top_p: Tuple[float, ...]  # one or several p values (a sweep)
+    k_min: int
+    refill_per_mille: int = 0
+    seed: int = 0
+    heads: str = "tau1"  # head-amplitude recipe, see _head_amplitudes
+    tile: Optional[Tuple[int, int]] = None  # spatial tile (rows, cols); None -> default
+    description: str = ""
+
+    @property
+    def seq_len(self) -> int:
+        t, h, w = self.grid
+        return t * h * w
+
+    @property
+    def tile_hw(self) -> Tuple[int, int]:
+        if self.tile is not None:
+            return self.tile
+        # One full spatial tile holds exactly one block of tokens.
+        return (8, 8) if self.block == 64 else (8, 16)
+
+    @property
+    def num_blocks(self) -> int:
+        return -(-self.seq_len // self.block)
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", 1, 64, (4, 16, 16), 64, (0.9,), 2, 0, seed=0, heads="tau1",
+        description="1 head, d=64, 1024 tokens on 4x16x16, block 64, p=0.9, k_min=2"),
+    "two_head": Workload(
+        "two_head", 2, 128, (4, 32, 32), 64, (0.9,), 4, 0, seed=1, heads="conc_flat",
+        description="2 heads, d=128, 4096 tokens on 4x32x32, block 64, p=0.9, k_min=4; "
+                    "head 0 locality x3, head 1 pure noise"),
+    "rank480p": Workload(
+        "rank480p", 5, 128, (21, 30, 52), 128, (0.95,), 8, 0, seed=2, heads="lograndom",
+        description="5 heads, d=128, 32760 tokens on 21x30x52, block 128, p=0.95, k_min=8; "
+                    "tau log-uniform in [0.3, 3]"),
+    "rank720p": Workload(
+        "rank720p", 5, 128, (21, 45, 80), 128, (0.95,), 8, 0, seed=3, heads="lograndom+flat",
+        description="5 heads, d=128, 75600 tokens on 21x45x80, block 128, p=0.95, k_min=8; "
+                    "heads 0-3 tau log-uniform, head 4 near-dense"),
+    "long115k": Workload(
+        "long115k", 3, 128, (33, 55, 64), 128, (0.8, 0.9, 0.95, 0.99), 8, 100, seed=4,
+        heads="lograndom",
+        description="3 heads, d=128, 116160 tokens on 33x55x64, block 128, p sweep, k_min=8, "
+                    "refill 100 per mille"),
+}
+
+WORKLOAD_ORDER = ["tiny", "two_head", "rank480p", "rank720p", "long115k"]
+
+
+def get_workload(name: str, **overrides) -> Workload:
+    base = WORKLOADS[name]
+    return dataclasses.replace(base, **overrides) if overrides else base
+
+
+@dataclasses.dataclass
+class Inputs:
+    workload: Workload
+    q: np.ndarray  # uint16 bf16 bits [H][N][d]
+    k: np.ndarray
+    v: np.ndarray
+    amps: np.ndarray  # locality amplitude per head
+    taus: np.ndarray  # temperature per head (inf for a flat head)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round-to-nearest-even), return uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _amp(tau: float, d: int) -> float:
+    return float(np.sqrt(BETA * np.sqrt(d) / tau))
+
+
+def _stratified_taus(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n log-uniform draws in TAU_RANGE, one per equal-width stratum, shuffled."""
+    lo, hi = np.log(TAU_RANGE[0]), np.log(TAU_RANGE[1])
+    u = (np.arange(n) + rng.random(n)) / n
+    taus = np.exp(lo + u * (hi - lo))
+    return taus[rng.permutation(n)]
+
+
+def _head_amplitudes(wl: Workload, rng: np.random.Generator):
+    H, d = wl.num_heads, wl.head_dim
+    if wl.heads == "tau1":
+        taus = np.ones(H)
+    elif wl.heads == "flat":
+        taus = np.full(H, np.inf)
+    elif wl.heads == "conc_flat":
+        taus = np.array([1.0] + [np.inf] * (H - 1))
+    elif wl.heads == "lograndom":
+        taus = _stratified_taus(rng, H)
+    elif wl.heads == "lograndom+flat":
+        taus = np.concatenate([_stratified_taus(rng, H - 1), [np.inf]])
+    else:
+        raise ValueError(f"unknown head recipe {wl.heads!r}")
+    amps = np.array([0.0 if np.isinf(t) else _amp(t, d) for t in taus])
+    if wl.heads == "conc_flat":
+        amps[0] *= 3.0  # the concentrated head: locality term scaled x3
+    return amps, taus
+
+
+def locality_features(grid, d: int, rng: np.random.Generator) -> np.ndarray:
+    """Random Fourier features of the (t, y, x) grid coordinate, [N][d] float64."""
+    T, Hh, W = grid
+    omega = rng.standard_normal((d, 3)) / SIGMA
+    phase = rng.uniform(0.0, 2.0 * np.pi, size=d)
+    n = np.arange(T * Hh * W)
+    coords = np.stack([n // (Hh * W), (n // W) % Hh, n % W], axis=1).astype(np.float64)
+    return np.sqrt(2.0 / d) * np.cos(coords @ omega.T + phase)
+
+
+def _generate(wl: Workload) -> Inputs:
+    rng = np.random.default_rng(wl.seed)
+    amps, taus = _head_amplitudes(wl, rng)
+    N, d, H = wl.seq_len, wl.head_dim, wl.num_heads
+    phi = locality_features(wl.grid, d, rng)
+    q = np.empty((H, N, d), np.uint16)
+    k = np.empty((H, N, d), np.uint16)
+    v = np.empty((H, N, d), np.uint16)
+    for h in range(H):
+        xq = rng.standard_normal((N, d))
+        xk = rng.standard_normal((N, d))
+        xv = rng.standard_normal((N, d))
+        q[h] = f32_to_bf16_bits((xq + amps[h] * phi).astype(np.float32))
+        k[h] = f32_to_bf16_bits((xk + amps[h] * phi).astype(np.float32))
+        v[h] = f32_to_bf16_bits(xv.astype(np.float32))
+    return Inputs(wl, q, k, v, amps, taus)
+
+
+@functools.lru_cache(maxsize=4)
+def _cached(wl: Workload) -> Inputs:
+    return _generate(wl)
+
+
+def make_inputs(wl: Workload, cache: bool = True) -> Inputs:
+    """Deterministic inputs for a workload (same seed -> same bits)."""
+    return _cached(wl) if cache else _generate(wl)
