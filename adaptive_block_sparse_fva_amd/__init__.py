@@ -1,0 +1,20 @@
+"""Adaptive block-sparse self-attention for video DiTs on AMD Instinct MI355X.
+
+The hot path lives in libfva.so (hand-written HIP for gfx950, C ABI in
+include/fva.h); `adaptive_block_sparse_fva_amd.fva` is its ctypes binding.
+"""
+
+from .fva import (  # noqa: F401
+    Buffers,
+    FvaError,
+    Problem,
+    attn_workgroups,
+    load_library,
+    make_problem,
+    plan,
+    route,
+    sizes,
+    sparse_attn_fwd,
+)
+
+__version__ = "0.1.0"

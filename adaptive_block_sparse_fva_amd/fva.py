@@ -1,0 +1,252 @@
+"""ctypes binding of libfva.so: the C ABI in include/fva.h, argument marshalling only.
+
+Every step of the routing, plan and attention runs in the library's HIP
+kernels; this module only turns torch tensors into device pointers and the
+current HIP stream into a handle, and raises on a non-zero status.  It refuses
+to run (FvaError) when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libfva.so")
+
+FVA_OK = 0
+FVA_ERR_ARG = 1
+FVA_ERR_UNSUPPORTED = 2
+FVA_ERR_HIP = 3
+FVA_ERR_WORKSPACE = 4
+FVA_MAX_BLOCKS = 2048
+FVA_MAX_TILES = 16384
+
+EXPORTED = (
+    "fva_sizes",
+    "fva_attn_workgroups",
+    "fva_route",
+    "fva_plan",
+    "fva_sparse_attn_fwd",
+    "fva_status_string",
+    "fva_last_error",
+    "fva_version",
+)
+
+
+class FvaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: status {status}" + (f" ({detail})" if detail else ""))
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("grid_t", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("tile_h", ctypes.c_int32),
+        ("tile_w", ctypes.c_int32),
+        ("top_p", ctypes.c_float),
+        ("k_min", ctypes.c_int32),
+        ("refill_per_mille", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("stride_head", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+    ]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("order_elems", ctypes.c_int64),
+        ("scores_elems", ctypes.c_int64),
+        ("ranked_elems", ctypes.c_int64),
+        ("col_idx_capacity", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("tile_counter_elems", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfva.so (once).  Raises FvaError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FvaError(-1, "load_library",
+                       f"{path} not built; run `python -m adaptive_block_sparse_fva_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp = ctypes.c_void_p
+    lib.fva_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
+    lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_status_string.argtypes = [ctypes.c_int]
+    lib.fva_status_string.restype = ctypes.c_char_p
+    lib.fva_last_error.argtypes = []
+    lib.fva_last_error.restype = ctypes.c_char_p
+    lib.fva_version.argtypes = []
+    for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
+                 "fva_sparse_attn_fwd", "fva_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != FVA_OK:
+        lib = load_library()
+        detail = lib.fva_status_string(status).decode()
+        if status == FVA_ERR_HIP:
+            detail += ": " + lib.fva_last_error().decode()
+        raise FvaError(status, where, detail)
+
+
+def make_problem(num_heads: int, seq_len: int, head_dim: int, grid: Sequence[int], block: int,
+                 tile: Sequence[int], top_p: float, k_min: int, refill_per_mille: int = 0,
+                 sm_scale: float = 0.0, stride_head: Optional[int] = None,
+                 stride_token: Optional[int] = None) -> Problem:
+    """Problem struct; default strides describe contiguous [H][N][d] tensors."""
+    if stride_token is None:
+        stride_token = head_dim
+    if stride_head is None:
+        stride_head = seq_len * stride_token
+    return Problem(num_heads, seq_len, head_dim, grid[0], grid[1], grid[2], block, tile[0],
+                   tile[1], float(top_p), k_min, refill_per_mille, float(sm_scale), stride_head,
+                   stride_token)
+
+
+def sizes(prob: Problem) -> Sizes:
+    out = Sizes()
+    _check(load_library().fva_sizes(ctypes.byref(prob), ctypes.byref(out)), "fva_sizes")
+    return out
+
+
+def attn_workgroups(prob: Problem) -> int:
+    out = ctypes.c_int32(0)
+    _check(load_library().fva_attn_workgroups(ctypes.byref(prob), ctypes.byref(out)),
+           "fva_attn_workgroups")
+    return int(out.value)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise FvaError(FVA_ERR_ARG, "binding", "tensors must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def route(prob, q, k, scores, ranked, row_count, head_count, order, workspace, stream=None):
+    st = load_library().fva_route(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(scores), _ptr(ranked),
+                                  _ptr(row_count), _ptr(head_count), _ptr(order), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "fva_route")
+
+
+def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, tile_order, tile_counter,
+         stream=None):
+    st = load_library().fva_plan(ctypes.byref(prob), _ptr(ranked), _ptr(row_count), _ptr(row_ptr),
+                                 _ptr(col_idx), _ptr(head_count_final), _ptr(tile_order),
+                                 _ptr(tile_counter), _stream(stream))
+    _check(st, "fva_plan")
+
+
+def sparse_attn_fwd(prob, q, k, v, order, row_ptr, col_idx, tile_order, tile_counter, o,
+                    lse=None, stream=None):
+    st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(order), _ptr(row_ptr), _ptr(col_idx),
+                                            _ptr(tile_order), _ptr(tile_counter), _ptr(o),
+                                            _ptr(lse), _stream(stream))
+    _check(st, "fva_sparse_attn_fwd")
+
+
+@dataclass
+class Buffers:
+    """Every device buffer one call of the hot path needs, allocated with torch."""
+
+    prob: Problem
+    nb: int
+    scores: torch.Tensor
+    ranked: torch.Tensor
+    row_count: torch.Tensor
+    head_count: torch.Tensor
+    order: torch.Tensor
+    workspace: torch.Tensor
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    head_count_final: torch.Tensor
+    tile_order: torch.Tensor
+    tile_counter: torch.Tensor
+    o: torch.Tensor
+    lse: torch.Tensor
+
+    @classmethod
+    def allocate(cls, prob: Problem, device="cuda") -> "Buffers":
+        sz = sizes(prob)
+        H, N, d = prob.num_heads, prob.seq_len, prob.head_dim
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(
+            prob=prob,
+            nb=sz.num_blocks,
+            scores=torch.empty(sz.scores_elems, dtype=torch.float32, device=device),
+            ranked=torch.empty(sz.ranked_elems, dtype=torch.int16, device=device),
+            row_count=torch.empty(sz.num_rows, **i32),
+            head_count=torch.empty(H, **i32),
+            order=torch.empty(sz.order_elems, **i32),
+            workspace=torch.empty(max(16, sz.workspace_bytes) // 4, dtype=torch.float32,
+                                  device=device),
+            row_ptr=torch.empty(sz.num_rows + 1, **i32),
+            col_idx=torch.empty(sz.col_idx_capacity, **i32),
+            head_count_final=torch.empty(H, **i32),
+            tile_order=torch.empty(sz.num_rows, **i32),
+            tile_counter=torch.zeros(sz.tile_counter_elems, **i32),
+            o=torch.empty((H, N, d), dtype=torch.bfloat16, device=device),
+            lse=torch.empty((H, N), dtype=torch.float32, device=device),
+        )
+
+    def route(self, q, k, stream=None):
+        route(self.prob, q, k, self.scores, self.ranked, self.row_count, self.head_count,
+              self.order, self.workspace, stream)
+
+    def plan(self, stream=None):
+        plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
+             self.head_count_final, self.tile_order, self.tile_counter, stream)
+
+    def attn(self, q, k, v, tile_order=None, with_lse=True, stream=None):
+        sparse_attn_fwd(self.prob, q, k, v, self.order, self.row_ptr, self.col_idx,
+                        self.tile_order if tile_order is None else tile_order, self.tile_counter,
+                        self.o, self.lse if with_lse else None, stream)
+
+    def run(self, q, k, v, stream=None):
+        """One full call of the hot path: route -> plan -> attention."""
+        self.route(q, k, stream)
+        self.plan(stream)
+        self.attn(q, k, v, stream=stream)
+        return self.o
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,189 @@
+/*
+ * fva.h -- C ABI of the adaptive block-sparse attention library (libfva.so)
+ * for video diffusion transformers on AMD Instinct MI355X (gfx950).
+ *
+ * One call of the hot path is three stream-ordered entry points:
+ *
+ *   fva_route            video-aware order, pooled Q/K block scores, ranking,
+ *                        Top-p cutoff with a Top-k floor, per-head counts
+ *   fva_plan             refill of next-ranked blocks, CSR block mask,
+ *                        heaviest-first (LPT) tile order, queue reset
+ *   fva_sparse_attn_fwd  block-sparse attention forward over the kept blocks,
+ *                        run from a persistent tile queue
+ *
+ * Sources (page title, section) for what each call computes:
+ *   "FVAttn: Adaptive Sparse Attention with Runtime Load Balancing for Video
+ *    Generation": S2.1 (scores s_{h,i,j}, mask M_{h,i,j}, Top-p, Top-k floor),
+ *    S2.2 Eq 1 (per-head workload), S3.1 (reordering, pooled Q/K similarity,
+ *    density and ranking from the same routing pass), S3.2 (runtime load
+ *    balancing moves work without changing it), S3.3 (slack-aware
+ *    augmentation adds next-ranked blocks without re-sorting).
+ *   "Sparse Attention for Video Generation Acceleration via Growing Sparsity
+ *    and Reduced Search": S3.2 (block-sparse FlashAttention skips unselected
+ *    key blocks), S5.3 (importance normalised per query block), A.1 (online
+ *    softmax), A.4 (shortest descending prefix reaching p), A.6 (reordering).
+ *
+ * Conventions
+ *   - Every buffer is allocated, owned and freed by the caller.  The library
+ *     never allocates, frees or synchronises; all work is enqueued on
+ *     `stream` (a hipStream_t, NULL = the default stream) and results are
+ *     valid once the caller has synchronised that stream.
+ *   - "device" pointers must point to memory of the current HIP device; the
+ *     problem struct is read on the host during the call only.
+ *   - Tensors q, k, v, o are bf16, element (h, n, c) at
+ *     h*stride_head + n*stride_token + c, in natural token order
+ *     n = t*grid_h*grid_w + y*grid_w + x.  They must be 16-byte aligned with
+ *     stride_token and stride_head multiples of 8 elements.
+ *   - Notation: H heads, N tokens, d head_dim, B block, nb = ceil(N/B) query
+ *     blocks = key blocks, H*nb (head, query-block) rows = tiles.
+ *   - Every entry point returns FVA_OK or an error code and never throws.
+ *     Argument checks run on the host before anything is enqueued; on an
+ *     error nothing is enqueued.  FVA_ERR_HIP means a launch failed; the
+ *     text is available from fva_last_error().
+ *   - The functions keep no state between calls and may be called from
+ *     several host threads; calls that share output buffers or the tile
+ *     counter must be ordered by the caller.
+ */
+#ifndef FVA_H_
+#define FVA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fva_status {
+  FVA_OK = 0,
+  FVA_ERR_ARG = 1,          /* null pointer, inconsistent sizes, NaN p, ... */
+  FVA_ERR_UNSUPPORTED = 2,  /* head_dim or block not in {64, 128}; size limits */
+  FVA_ERR_HIP = 3,          /* a HIP launch or device query failed */
+  FVA_ERR_WORKSPACE = 4     /* workspace smaller than fva_sizes() asks for */
+};
+
+/* Largest supported nb (key blocks per row) and H*nb (rows / tiles). */
+#define FVA_MAX_BLOCKS 2048
+#define FVA_MAX_TILES 16384
+
+/*
+ * The problem statement (FVAttn S2.1: per head h, query block i, key block j;
+ * Top-p threshold p and Top-k floor; S3.1: video-aware block organisation).
+ */
+typedef struct fva_problem {
+  int32_t num_heads;         /* H >= 1 */
+  int32_t seq_len;           /* N, must equal grid_t * grid_h * grid_w */
+  int32_t head_dim;          /* d in {64, 128} */
+  int32_t grid_t, grid_h, grid_w; /* latent video grid, each >= 1 */
+  int32_t block;             /* B in {64, 128}; query and key blocks alike */
+  int32_t tile_h, tile_w;    /* spatial tile of the order; both 0 = raster order */
+  float top_p;               /* p; >= 1 keeps every block, <= 0 keeps only the floor */
+  int32_t k_min;             /* Top-k floor >= 1 (clamped to nb) */
+  int32_t refill_per_mille;  /* one-GPU slack refill, 0..1000 (0 = off) */
+  float sm_scale;            /* softmax scale; 0 = 1/sqrt(d) */
+  int64_t stride_head;       /* elements between heads in q, k, v, o */
+  int64_t stride_token;      /* elements between tokens (>= d) */
+} fva_problem;
+
+/* Sizes derived from a problem (element counts unless named _bytes). */
+typedef struct fva_sizes_t {
+  int32_t num_blocks;        /* nb */
+  int32_t num_rows;          /* H*nb: row_count, tile_order, row_ptr - 1 */
+  int64_t order_elems;       /* nb*B int32 (order) */
+  int64_t scores_elems;      /* H*nb*nb float (scores) */
+  int64_t ranked_elems;      /* H*nb*nb int16 (ranked) */
+  int64_t col_idx_capacity;  /* H*nb*nb int32 (col_idx, worst case) */
+  int64_t workspace_bytes;   /* fva_route workspace */
+  int32_t tile_counter_elems;/* 2 uint32 */
+} fva_sizes_t;
+
+/* Host only: validate a problem and report buffer sizes.  Makes no HIP call. */
+int fva_sizes(const fva_problem* prob, fva_sizes_t* out);
+
+/* Number of persistent workgroups fva_sparse_attn_fwd launches for this
+ * problem on the current device (compute units x resident workgroups per
+ * unit, at most H*nb).  Queries the device; FVA_ERR_HIP without one. */
+int fva_attn_workgroups(const fva_problem* prob, int32_t* out);
+
+/*
+ * Routing frontend (FVAttn S3.1; GSRS S5.3, A.4, A.6).
+ *   q, k        device bf16 [H][N][d] (strided as above), read only.
+ *   scores      device float [H][nb][nb], written: s_{h,i,j} =
+ *               sm_scale * <mean of Q_h over query block i, mean of K_h over
+ *               key block j>, blocks taken in the video-aware order.
+ *   ranked      device int16 [H][nb][nb], written: per row, key-block ids by
+ *               float32 score descending, equal scores by lower id.
+ *   row_count   device int32 [H*nb], written: k_i = max(k_p, min(k_min, nb))
+ *               where k_p is the shortest ranked prefix whose importance
+ *               (softmax of the row's scores, as exact 2^-40 fixed-point
+ *               weights) reaches p.
+ *   head_count  device int32 [H], written: sum of row_count over the head's
+ *               rows (Eq 1: L_h = head_count[h] / nb).
+ *   order       device int32 [nb*B], written: natural token index of every
+ *               position of the video-aware order, -1 past N (frame-major,
+ *               tile_h x tile_w tiles in raster order, raster inside a tile,
+ *               edge tiles cut at the border).
+ *   workspace   device scratch of workspace_bytes >= fva_sizes().workspace_bytes
+ *               (pooled block means); contents are not needed after the call.
+ */
+int fva_route(const fva_problem* prob, const void* q, const void* k,
+              float* scores, int16_t* ranked, int32_t* row_count,
+              int32_t* head_count, int32_t* order,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Plan (FVAttn S3.2-S3.3 on one GPU: the placement step becomes a
+ * heaviest-first tile queue, slack augmentation a per-row refill).
+ *   ranked, row_count   as written by fva_route, read only.
+ *   row_ptr      device int32 [H*nb + 1], written: CSR row offsets of the
+ *                final mask; row (h, i) keeps k'_i = k_i + e_i blocks with
+ *                e_i = min(nb - k_i, floor(k_i * refill_per_mille / 1000)).
+ *   col_idx      device int32 [>= row_ptr[H*nb]] (capacity H*nb*nb always
+ *                suffices), written: the first k'_i ranked key blocks of each
+ *                row, ascending.
+ *   head_count_final  device int32 [H], written: sum of k'_i per head.
+ *   tile_order   device int32 [H*nb], written: tile ids h*nb + i sorted by
+ *                k'_i descending, then h, then i.
+ *   tile_counter device uint32 [2], written: reset to {0, 0}.
+ */
+int fva_plan(const fva_problem* prob, const int16_t* ranked,
+             const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
+             int32_t* head_count_final, int32_t* tile_order,
+             uint32_t* tile_counter, void* stream);
+
+/*
+ * Block-sparse attention forward (GSRS S3.2, A.1): for every query token of
+ * query block i of head h, softmax(sm_scale * q.k) over the tokens of the kept
+ * key blocks col_idx[row_ptr[h*nb+i] .. row_ptr[h*nb+i+1]) only, times V.
+ *   q, k, v      device bf16, read only.
+ *   order        device int32 [nb*B] as written by fva_route.
+ *   row_ptr, col_idx   CSR mask (each row non-empty, ids in [0, nb)).
+ *   tile_order   device int32 [H*nb], a permutation of the tile ids; the
+ *                queue hands tiles out in this order.  Any permutation gives
+ *                bitwise the same o and lse.
+ *   tile_counter device uint32 [2], must be {0, 0} on entry (fva_plan leaves
+ *                it so); the kernel leaves it {0, 0} again on exit.
+ *   o            device bf16 [H][N][d] (strided like q), written.
+ *   lse          device float [H][N] or NULL, written: natural-log
+ *                log-sum-exp of each query's kept logits.
+ */
+int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* k,
+                        const void* v, const int32_t* order,
+                        const int32_t* row_ptr, const int32_t* col_idx,
+                        const int32_t* tile_order, uint32_t* tile_counter,
+                        void* o, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* fva_status_string(int status);
+
+/* Text of the last FVA_ERR_HIP on the calling thread ("" if none). */
+const char* fva_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fva_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* FVA_H_ */

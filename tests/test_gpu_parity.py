@@ -1,0 +1,201 @@
+"""GPU parity: the HIP chain (through the C ABI) against the fp64 oracle.
+
+Routing and plan outputs are integers and must match bit for bit (the oracle
+selects from the GPU's exported fp32 scores, so both sides decide from the
+same numbers); scores match the oracle's fp64 scores to 1e-4 relative;
+attention outputs are within max-abs 2e-2 / mean-abs 2e-3 of an fp64 masked
+softmax, LSE within 1e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import (LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, S_REL, device_inputs, f64_inputs,
+                         problem_for, run_chain, sample_tiles, say, tile_rows)
+from synth import WORKLOADS, Workload, make_inputs
+from synth.workloads import WORKLOAD_ORDER
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(name, p) for name in WORKLOAD_ORDER for p in WORKLOADS[name].top_p]
+FULL_ATTENTION = {"tiny", "two_head"}
+
+
+def _oracle_scores(wl, inp):
+    q64, k64, _ = f64_inputs(inp)
+    order = O.token_order(wl.grid, wl.tile_hw)
+    return O.block_scores(O.pool(q64, order, wl.block), O.pool(k64, order, wl.block),
+                          1.0 / math.sqrt(wl.head_dim))
+
+
+def check_routing_and_plan(wl, inp, res, p, refill):
+    H, nb = wl.num_heads, res["nb"]
+    # order: closed form on the GPU vs enumeration in the oracle
+    np.testing.assert_array_equal(
+        res["order"], O.padded_order(O.token_order(wl.grid, wl.tile_hw), wl.block))
+    # scores: fp32 MFMA vs fp64
+    s64 = _oracle_scores(wl, inp)
+    err = np.abs(res["scores"].astype(np.float64) - s64).max()
+    assert err <= S_REL * np.abs(s64).max(), f"score error {err}"
+    # ranking, counts: bit-exact from the GPU's own fp32 scores
+    S32 = res["scores"]
+    for r in range(H * nb):
+        h, i = divmod(r, nb)
+        np.testing.assert_array_equal(res["ranked"][r], O.ranking(S32[h, i]), err_msg=f"row {r}")
+    rc, hc = O.select_counts(S32, p, wl.k_min)
+    np.testing.assert_array_equal(res["row_count"], rc)
+    np.testing.assert_array_equal(res["head_count"], hc)
+    # the oracle's own scores rounded to fp32 give the same counts except on rows
+    # whose cutoff sits within rounding of p (reported, expected zero or near)
+    rc_own, _ = O.select_counts(s64.astype(np.float32), p, wl.k_min)
+    say(f"  rows whose count differs under the oracle's own scores: {int((rc_own != rc).sum())}"
+        f" of {H * nb}")
+    pl = O.plan(S32, rc, refill)
+    np.testing.assert_array_equal(res["row_ptr"], pl["row_ptr"])
+    np.testing.assert_array_equal(res["col_idx"], pl["col_idx"])
+    np.testing.assert_array_equal(res["head_count_final"], pl["head_count"])
+    np.testing.assert_array_equal(res["tile_order"], pl["tile_order"])
+    np.testing.assert_array_equal(res["tile_counter"], [0, 0])
+    return pl
+
+
+def check_attention(wl, inp, res, tiles=None, label=""):
+    q64, k64, v64 = f64_inputs(inp)
+    order = O.token_order(wl.grid, wl.tile_hw)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    o_ref, lse_ref = O.masked_attention(q64, k64, v64, order, wl.block, res["row_ptr"],
+                                        res["col_idx"], scale, tiles)
+    if tiles is None:
+        do = np.abs(res["o"] - o_ref)
+        dl = np.abs(res["lse"] - lse_ref)
+    else:
+        rows = tile_rows(order, wl.block, wl.seq_len, tiles, res["nb"])
+        do = np.concatenate([np.abs(res["o"][h, r] - o_ref[h, r]).ravel() for h, r in rows.items()])
+        dl = np.concatenate([np.abs(res["lse"][h, r] - lse_ref[h, r]).ravel() for h, r in rows.items()])
+    say(f"  {label} O max-abs {do.max():.3e} mean-abs {do.mean():.3e}; LSE max-abs {dl.max():.3e}")
+    assert np.all(np.isfinite(do))
+    assert do.max() <= O_MAX_ABS
+    assert do.mean() <= O_MEAN_ABS
+    assert dl.max() <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("name,p", CASES, ids=[f"{n}-p{p}" for n, p in CASES])
+def test_chain_matches_oracle(name, p):
+    wl = WORKLOADS[name]
+    say(f"[gpu] chain {name} p={p} H={wl.num_heads} N={wl.seq_len} d={wl.head_dim} B={wl.block}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, p), q, k, v)
+    check_routing_and_plan(wl, inp, res, p, wl.refill_per_mille)
+    if name in FULL_ATTENTION:
+        check_attention(wl, inp, res, label="all tiles:")
+    else:
+        tiles = sample_tiles(res["row_ptr"], wl.num_heads, res["nb"], per_head=12, seed=7)
+        check_attention(wl, inp, res, tiles, label=f"{len(tiles)} sampled tiles:")
+
+
+@pytest.mark.parametrize("name", ["tiny", "two_head"])
+def test_p_one_is_dense_attention(name):
+    wl = WORKLOADS[name]
+    say(f"[gpu] dense p=1 {name}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, 1.0), q, k, v)
+    nb = res["nb"]
+    assert np.all(res["row_count"] == nb)
+    q64, k64, v64 = f64_inputs(inp)
+    o_ref, lse_ref = O.dense_attention(q64, k64, v64, 1.0 / math.sqrt(wl.head_dim))
+    do = np.abs(res["o"] - o_ref)
+    say(f"  dense O max-abs {do.max():.3e} mean-abs {do.mean():.3e}")
+    assert do.max() <= O_MAX_ABS and do.mean() <= O_MEAN_ABS
+    assert np.abs(res["lse"] - lse_ref).max() <= LSE_MAX_ABS
+
+
+def test_p_zero_is_pure_top_k():
+    wl = WORKLOADS["two_head"]
+    say("[gpu] p=0 -> Top-k_min")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, 0.0), q, k, v)
+    assert np.all(res["row_count"] == wl.k_min)
+    check_routing_and_plan(wl, inp, res, 0.0, 0)
+    check_attention(wl, inp, res, label="top-k:")
+
+
+@pytest.mark.parametrize("name", ["two_head", "rank480p"])
+def test_tile_order_changes_placement_only(name):
+    """Any queue order gives bitwise the same output (placement, not computation)."""
+    wl = WORKLOADS[name]
+    say(f"[gpu] LPT vs natural tile order {name}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    buf, res = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
+    natural = torch.arange(buf.tile_order.numel(), dtype=torch.int32, device="cuda")
+    reverse = torch.flip(natural, [0])
+    for alt in (natural, reverse):
+        buf.attn(q, k, v, tile_order=alt)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.o.view(torch.int16).cpu(), torch.from_numpy(
+            res["o"].astype(np.float32)).to(torch.bfloat16).view(torch.int16))
+        np.testing.assert_array_equal(buf.lse.cpu().numpy(), res["lse"].astype(np.float32))
+        assert buf.tile_counter.cpu().tolist() == [0, 0]
+
+
+def test_repeat_calls_are_deterministic():
+    wl = WORKLOADS["rank480p"]
+    say("[gpu] determinism rank480p")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, a = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
+    _, b = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
+    for key in ("order", "scores", "ranked", "row_count", "row_ptr", "col_idx", "tile_order",
+                "o", "lse"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+EDGE = [
+    # name, heads, d, grid, block, tile, p, k_min, refill, recipe
+    ("one_short_block", 2, 64, (1, 5, 7), 64, (8, 8), 0.9, 2, 0, "tau1"),
+    ("ragged_tail", 2, 128, (3, 9, 11), 64, (8, 8), 0.8, 1, 0, "conc_flat"),
+    ("raster_order", 1, 64, (2, 10, 20), 128, (0, 0), 0.9, 1, 0, "tau1"),
+    ("d64_b128", 3, 64, (4, 24, 32), 128, (8, 16), 0.95, 3, 250, "lograndom"),
+    ("kmin_above_nb", 2, 128, (2, 16, 16), 64, (8, 8), 0.5, 100, 0, "conc_flat"),
+    ("refill_full", 2, 128, (4, 16, 24), 64, (8, 8), 0.7, 2, 1000, "lograndom"),
+    ("odd_tiles", 2, 128, (3, 13, 29), 64, (5, 7), 0.9, 2, 100, "lograndom"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(case):
+    name, H, d, grid, block, tile, p, kmin, refill, recipe = case
+    wl = Workload(name, H, d, grid, block, (p,), kmin, refill, seed=11, heads=recipe, tile=tile)
+    say(f"[gpu] edge {name} N={wl.seq_len} nb={wl.num_blocks}")
+    inp = make_inputs(wl, cache=False)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, p), q, k, v)
+    check_routing_and_plan(wl, inp, res, p, refill)
+    check_attention(wl, inp, res, label=name)
+
+
+def test_token_major_layout_matches_head_major():
+    """q/k/v/o given as [N][H][d] (heads interleaved, as a DiT projection emits)."""
+    wl = WORKLOADS["two_head"]
+    say("[gpu] token-major strides")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, ref = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
+    H, N, d = q.shape
+    qt, kt, vt = (x.permute(1, 0, 2).contiguous() for x in (q, k, v))
+    prob = problem_for(wl, wl.top_p[0], stride_head=d, stride_token=H * d)
+    import adaptive_block_sparse_fva_amd as F
+    buf = F.Buffers.allocate(prob)
+    buf.o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    buf.run(qt, kt, vt)
+    torch.cuda.synchronize()
+    got = buf.o.permute(1, 0, 2).float().cpu().numpy()
+    np.testing.assert_array_equal(got, ref["o"])
+    np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
