@@ -1,0 +1,260 @@
+"""Benchmark of one adaptive block-sparse attention call on one MI355X.
+
+A step is one whole call of the hot path on resident inputs: fva_route
+(order, pooled scores, ranking, Top-p + floor) -> fva_plan (refill, CSR, LPT
+order) -> fva_sparse_attn_fwd.  The default workload is one rank's share of a
+480p-style video DiT layer: 5 heads x 32,760 tokens (21 x 30 x 52 latent grid),
+head_dim 128, block 128, p = 0.95, k_min = 8.
+
+Prints ONE JSON line (see the keys below).  `--gpus N` with N > 1 exits: this
+build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("ms/attention call + dense-equiv TFLOPS; kept-block MFMA util at 5 heads×32K tokens")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rank480p")
+    ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle's attention sample")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-dense", action="store_true")
+    return ap.parse_args()
+
+
+def kept_flops_and_pairs(row_ptr, col_idx, n_tokens, block, head_dim, num_heads, nb):
+    import numpy as np
+    sizes = np.minimum(block, n_tokens - np.arange(nb) * block).astype(np.int64)
+    col_sizes = sizes[col_idx]
+    per_row = np.add.reduceat(col_sizes, row_ptr[:-1]) if len(col_idx) else np.zeros(len(row_ptr) - 1)
+    q_sizes = np.tile(sizes, num_heads)
+    return int(4 * head_dim * int((q_sizes * per_row).sum())), int(len(col_idx))
+
+
+def list_schedule_makespan(costs, workers):
+    """Greedy list scheduling (each tile to the earliest-free worker)."""
+    import heapq
+    heap = [0.0] * workers
+    heapq.heapify(heap)
+    for c in costs:
+        t = heapq.heappop(heap)
+        heapq.heappush(heap, t + float(c))
+    return max(heap)
+
+
+def cpu_baseline(wl, inp, p, gpu_o, row_ptr_gpu, col_idx_gpu, budget_s):
+    """The oracle as it stands, on the host cores: full routing + plan, and the
+    fp64 masked attention on a seeded sample of tiles bounded by budget_s."""
+    import numpy as np
+    import oracle as O
+    from synth import bf16_bits_to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    q64, k64, v64 = (bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+    t0 = time.perf_counter()
+    r = O.route(q64, k64, wl.grid, wl.tile_hw, wl.block, p, wl.k_min)
+    t1 = time.perf_counter()
+    pl = O.plan(r["scores32"], r["row_count"], wl.refill_per_mille)
+    t2 = time.perf_counter()
+    nb, H = wl.num_blocks, wl.num_heads
+    total_flops, _ = kept_flops_and_pairs(pl["row_ptr"], pl["col_idx"], wl.seq_len, wl.block,
+                                          wl.head_dim, H, nb)
+    rng = np.random.default_rng(123)
+    perm = rng.permutation(H * nb)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    done, flops, start = [], 0, time.perf_counter()
+    sizes = np.minimum(wl.block, wl.seq_len - np.arange(nb) * wl.block)
+    # attention on the GPU's own mask so that the sample doubles as a parity check
+    for t in perm:
+        o_ref, _ = O.masked_attention(q64, k64, v64, r["order"], wl.block, row_ptr_gpu, col_idx_gpu,
+                                      scale, [int(t)])
+        h, i = divmod(int(t), nb)
+        toks = r["order"][i * wl.block: min(wl.seq_len, (i + 1) * wl.block)]
+        err = np.abs(gpu_o[h, toks] - o_ref[h, toks])
+        done.append((err.max(), err.mean()))
+        cols = col_idx_gpu[row_ptr_gpu[t]: row_ptr_gpu[t + 1]]
+        flops += 4 * wl.head_dim * int(sizes[i]) * int(sizes[cols].sum())
+        if time.perf_counter() - start > budget_s:
+            break
+    t_attn_sample = time.perf_counter() - start
+    gpu_flops, _ = kept_flops_and_pairs(row_ptr_gpu, col_idx_gpu, wl.seq_len, wl.block,
+                                        wl.head_dim, H, nb)
+    t_attn_full = t_attn_sample * gpu_flops / max(flops, 1)
+    value_ms = (t1 - t0 + t2 - t1 + t_attn_full) * 1e3
+    errs = np.array(done)
+    return {
+        "value": round(value_ms, 1),
+        "unit": "ms",
+        "cores": blas_threads if blas_threads else cores,
+        "kind": "oracle",
+        "sample": (f"full routing+plan ({t1 - t0:.2f}s + {t2 - t1:.2f}s); fp64 masked attention on "
+                   f"{len(done)} of {H * nb} seeded-random tiles ({flops / 1e9:.1f} of "
+                   f"{gpu_flops / 1e9:.1f} GFLOP kept, {t_attn_sample:.1f}s), extrapolated by kept FLOPs"),
+        "host_cores_visible": cores,
+        "sample_parity": {"o_max_abs": float(errs[:, 0].max()), "o_mean_abs": float(errs[:, 1].mean()),
+                          "tiles": len(done)},
+        "oracle_matches_gpu_mask": bool(np.array_equal(pl["row_ptr"], row_ptr_gpu)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "head-migration path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import adaptive_block_sparse_fva_amd as F
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    p = args.top_p if args.top_p is not None else wl.top_p[0]
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl)
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    H, N, d, B = wl.num_heads, wl.seq_len, wl.head_dim, wl.block
+    prob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, p, wl.k_min, wl.refill_per_mille)
+    buf = F.Buffers.allocate(prob)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        buf.run(q, k, v)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        buf.route(q, k)
+        e[1].record(stream)
+        buf.plan()
+        e[2].record(stream)
+        buf.attn(q, k, v)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_route = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_plan = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_attn = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    total_ms = ev[0][0].elapsed_time(ev[-1][3])
+    ms_per_step = total_ms / K
+
+    nb = buf.nb
+    row_ptr = buf.row_ptr.cpu().numpy().astype(np.int64)
+    col_idx = buf.col_idx[: int(row_ptr[-1])].cpu().numpy().astype(np.int64)
+    head_final = buf.head_count_final.cpu().numpy()
+    kept, pairs = kept_flops_and_pairs(row_ptr, col_idx, N, B, d, H, nb)
+    dense_flops = 4.0 * N * N * d * H
+    attn_avg_ms = float(t_attn.mean())
+    achieved_tflops = kept / (attn_avg_ms * 1e-3) / 1e12
+    route_bytes = 2 * H * N * d * 2 + H * nb * nb * (4 + 2) + H * nb * 4 * 2 + nb * B * 4
+    route_gbs = route_bytes / (float(t_route.mean()) * 1e-3) / 1e9
+
+    # one-GPU analog of the load-imbalance factor: tiles list-scheduled onto the
+    # persistent workgroups, heaviest-first vs natural order
+    workers = F.attn_workgroups(prob)
+    costs = np.diff(row_ptr)
+    lpt = list_schedule_makespan(np.sort(costs)[::-1], workers)
+    natural = list_schedule_makespan(costs, workers)
+    ideal = costs.sum() / workers
+
+    dense = None
+    if not args.skip_dense:
+        dprob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, 1.0, wl.k_min, 0)
+        dbuf = F.Buffers.allocate(dprob)
+        dbuf.run(q, k, v)
+        dbuf.run(q, k, v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            dbuf.run(q, k, v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        dense = {"ms_per_call": round(dense_ms, 4),
+                 "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1),
+                 "sparse_speedup": round(dense_ms / ms_per_step, 3)}
+        del dbuf
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        gpu_o = buf.o.float().cpu().numpy().astype(np.float64)
+        cpu = cpu_baseline(wl, inp, p, gpu_o, row_ptr, col_idx, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Q/K/V with a grid-locality term; no model weights)",
+        "config": {"workload": wl.name, "heads": H, "seq_len": N, "grid": list(wl.grid),
+                   "head_dim": d, "block": B, "tile": list(wl.tile_hw), "top_p": p,
+                   "k_min": wl.k_min, "refill_per_mille": wl.refill_per_mille,
+                   "parallelism": "1 GPU (one Ulysses rank's head share)"},
+        "dense_equiv_tflops": round(dense_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "kept_block_mfma_util": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+        "density": round(pairs / (H * nb * nb), 4),
+        "head_density": [round(float(x) / (nb * nb), 4) for x in head_final],
+        "ms": {"route": round(float(t_route.mean()), 4), "plan": round(float(t_plan.mean()), 4),
+               "attn": round(attn_avg_ms, 4), "step_median": round(float(np.median(t_step)), 4),
+               "step_p10": round(float(np.percentile(t_step, 10)), 4),
+               "step_p90": round(float(np.percentile(t_step, 90)), 4),
+               "host_wall_per_step": round(wall / K * 1e3, 4)},
+        "route_hbm": {"bytes": route_bytes, "GB/s": round(route_gbs, 1),
+                      "frac": round(route_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "sparse_attn_fwd_kernel<128,128>",
+                     "algorithmic_flops_per_launch": kept},
+        "cu_imbalance": {"workgroups": workers, "lpt": round(lpt / ideal, 4),
+                         "natural": round(natural / ideal, 4)},
+        "dense_reference": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
