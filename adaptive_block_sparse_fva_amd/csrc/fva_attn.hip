@@ -15,11 +15,16 @@
 //     B = Q fragments kept in registers for the whole tile, so every lane owns
 //     one query column and the softmax row statistics stay in-lane (one
 //     cross-half shuffle for the maximum per block);
-//   - O^T += V^T P^T: A = V^T from LDS (V is transposed while staging),
-//     B = P converted to bf16 straight from the S^T accumulators; the key
-//     permutation implied by the accumulator layout is applied to the V^T
-//     reads, so no register shuffles are needed;
-//   - K and V rows are gathered through the order table (position -> token).
+//   - O^T += V^T P^T: A = V^T fragments read from row-major V in LDS with the
+//     transposing LDS load (ds_read_b64_tr_b16), B = P converted to bf16
+//     straight from the S^T accumulators; the key permutation implied by the
+//     accumulator layout is applied to the V^T reads, so no register shuffles
+//     are needed;
+//   - K and V rows are gathered through the order table (position -> token)
+//     into registers one block ahead and written to the other half of a
+//     double-buffered LDS tile while the current block is computed.
+#include <type_traits>
+
 #include "fva_common.h"
 
 namespace fva {
@@ -40,28 +45,60 @@ struct AttnArgs {
   float scale_log2;  // sm_scale * log2(e)
 };
 
+typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
+// source lane s fetches the 4 bf16 at its own address; destination lane i then
+// holds element i%4 of the chunks fetched by lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)lds_base, 16, 0, 0);
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = BLK / 32;  // waves per workgroup
-  constexpr int NT = NW * 64;   // threads per workgroup
   constexpr int KS = BLK / 32;  // 32-key sub-tiles of S^T
   constexpr int DS = D / 16;    // k-steps of S^T = K Q^T
   constexpr int DO = D / 32;    // 32-row sub-tiles of O^T
   constexpr int PS = BLK / 16;  // k-steps of O^T += V^T P^T
-  constexpr int KLD = D + 8;    // LDS row stride of K (elements)
-  constexpr int VLD = BLK + 4;  // LDS row stride of V^T (elements)
   constexpr int CH = D / 8;     // 16-byte chunks per K/V row
-  constexpr int GPI = NT / CH;  // 4-row groups staged per pass
-  constexpr int ITS = (BLK / 4) / GPI;
-  static_assert(ITS >= 1 && (BLK / 4) % GPI == 0, "staging layout");
+  constexpr int RW = 64 / CH;   // rows written by one wave-wide LDS-DMA load
+  constexpr int NI = 32 / RW;   // LDS-DMA loads per wave per tile (a wave stages 32 rows)
+  constexpr int TILE = BLK * D; // elements of one K or V tile
+  static_assert(NW * 32 == BLK, "one wave per 32 rows");
 
-  __shared__ __attribute__((aligned(16))) bf16_t ks[BLK * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[D * VLD];
+  // K and V tiles, rows of D elements, 16-byte chunk c of row r stored at
+  // chunk position c ^ (r % CH): the 32 rows an MFMA operand read touches at
+  // one logical chunk then fall into distinct banks.  Two buffers (0 and 1):
+  // the next key block streams in while the current one is used.  They are
+  // separate LDS objects and the block loop is unrolled by two, so the
+  // compiler can tell that loads into one buffer never alias reads of the
+  // other and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[TILE];
   __shared__ int s_tile;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  // staging role of this lane in a wave-wide LDS-DMA load
+  const int st_sub = lane / CH;          // row inside the load's RW rows
+  const int st_phys = lane % CH;         // chunk position it writes
 
   for (;;) {
     if (tid == 0) s_tile = (int)atomicAdd(&a.tile_counter[0], 1u);
@@ -97,44 +134,49 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int c0 = a.row_ptr[t], c1 = a.row_ptr[t + 1];
-    for (int c = c0; c < c1; ++c) {
-      const int j = a.col_idx[c];
-      __syncthreads();  // all waves are done reading the previous K/V tile
+    const int c0 = a.row_ptr[t], cnt = a.row_ptr[t + 1] - c0;
+    const int32_t* cols = a.col_idx + c0;
 
-      // ---- stage K (row-major) and V (transposed) of key block j in LDS ----
+    // Token index of each row this lane stages, one key block ahead.
+    // Positions past the end of the sequence (order = -1, last block only)
+    // stage token 0 instead: their keys are masked to -inf before the
+    // softmax, so their V rows are multiplied by exactly zero.
+    int toks[NI];
+    auto load_toks = [&](int j) {
 #pragma unroll
-      for (int it = 0; it < ITS; ++it) {
-        const int g = tid / CH + it * GPI;  // rows 4g .. 4g+3 of the block
-        const int ch = tid % CH;
-        const int32_t* tp = a.order + j * BLK + 4 * g;
-        const int t0 = tp[0], t1 = tp[1], t2 = tp[2], t3 = tp[3];
-        const int toks[4] = {t0, t1, t2, t3};
-        u32x4 kr[4], vr[4];
+      for (int m = 0; m < NI; ++m)
+        toks[m] = max(a.order[j * BLK + wave * 32 + m * RW + st_sub], 0);
+    };
+    auto issue = [&](bf16_t* kt, bf16_t* vt) {
+      kt += (wave * 32) * D;
+      vt += (wave * 32) * D;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          kr[rr] = u32x4{0u, 0u, 0u, 0u};
-          vr[rr] = u32x4{0u, 0u, 0u, 0u};
-          if (toks[rr] >= 0) {
-            const int64_t off = (int64_t)toks[rr] * a.stride_token + ch * 8;
-            kr[rr] = *reinterpret_cast<const u32x4*>(kh + off);
-            vr[rr] = *reinterpret_cast<const u32x4*>(vh + off);
-          }
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<u32x4*>(&ks[(4 * g + rr) * KLD + ch * 8]) = kr[rr];
-        // transpose 4 keys x 8 features into 8 rows of V^T, 4 keys each
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t w0 = vr[0][m], w1 = vr[1][m], w2 = vr[2][m], w3 = vr[3][m];
-          const u32x2 even = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-          const u32x2 odd = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-          *reinterpret_cast<u32x2*>(&vt[(ch * 8 + 2 * m) * VLD + 4 * g]) = even;
-          *reinterpret_cast<u32x2*>(&vt[(ch * 8 + 2 * m + 1) * VLD + 4 * g]) = odd;
-        }
+      for (int m = 0; m < NI; ++m) {
+        const int row = wave * 32 + m * RW + st_sub;
+        const int64_t off = (int64_t)toks[m] * a.stride_token + ((st_phys ^ (row & (CH - 1))) * 8);
+        lds_dma16(kh + off, kt + m * RW * D);
+        lds_dma16(vh + off, vt + m * RW * D);
       }
-      __syncthreads();
+    };
+
+    load_toks(cols[0]);
+    issue(k_lds0, v_lds0);
+    if (cnt > 1) load_toks(cols[1]);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // one key block: compute on buffer CUR while the next block streams into
+    // the other buffer
+    auto step = [&](auto cur_tag, int n) {
+      constexpr int CUR = decltype(cur_tag)::value;
+      const bf16_t* ks = CUR ? k_lds1 : k_lds0;
+      const bf16_t* vs = CUR ? v_lds1 : v_lds0;
+      const int j = cols[n];
+      if (n + 1 < cnt) {
+        if (CUR) issue(k_lds0, v_lds0);
+        else issue(k_lds1, v_lds1);
+        if (n + 2 < cnt) load_toks(cols[n + 2]);
+      }
 
       // ---- S^T = K Q^T for this wave's 32 queries ----
       f32x16 s[KS];
@@ -142,9 +184,11 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
+        const int row = kk * 32 + l32;
 #pragma unroll
         for (int d = 0; d < DS; ++d) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(&ks[(kk * 32 + l32) * KLD + d * 16 + hf * 8]);
+          const int phys = (2 * d + hf) ^ (row & (CH - 1));
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&ks[row * D + phys * 8]);
           s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[d], s[kk],
                                                           0, 0, 0);
         }
@@ -161,47 +205,69 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
             if (kk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) >= valid) s[kk][r] = -INFINITY;
       }
 
-      // ---- online softmax (base 2), row statistics per lane ----
+  // ---- online softmax (base 2), row statistics per lane ----
+      // The running maximum m_run is only raised when a block's maximum
+      // exceeds it by more than 8 (a factor 2^8), so most blocks skip the
+      // rescale of the accumulators; weights then stay below 2^8, and the
+      // final division by the matching denominator makes the result exact.
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+      if (__any(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DO; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(s[kk][r], a.scale_log2, -m_new));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][r], a.scale_log2, -m_run));
           s[kk][r] = p;
           rs += p;
         }
-      l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-      for (int d = 0; d < DO; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
+      l_run += rs;
 
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T; V^T fragments come from row-major V by
+      // transposing reads: source lane s16 of lane group g16 fetches keys
+      // ps*16 + 4*(g16/2) + s16/4 (and +8), features
+      // d*32 + 16*(g16%2) + 4*(s16%4), i.e. half (s16&1) of logical chunk
+      // d*4 + 2*(g16%2) + (s16%4)/2
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[ps >> 1][(ps & 1) * 8 + e];
+        const int vr0 = ps * 16 + 4 * (g16 >> 1) + (s16 >> 2);
+        const int vr1 = vr0 + 8;
 #pragma unroll
         for (int d = 0; d < DO; ++d) {
-          const bf16_t* vrow = &vt[(d * 32 + l32) * VLD + ps * 16 + hf * 4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const int c = d * 4 + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+          const u32x2 lo = lds_read_tr16(&vs[vr0 * D + ((c ^ (vr0 & (CH - 1))) * 8) + 4 * (s16 & 1)]);
+          const u32x2 hi = lds_read_tr16(&vs[vr1 * D + ((c ^ (vr1 & (CH - 1))) * 8) + 4 * (s16 & 1)]);
           const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
           acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf, acc_o[d],
                                                              0, 0, 0);
         }
       }
+
+      // the next block's LDS-DMA loads (and token loads) have landed for every
+      // wave, and every wave is done reading this block's buffer
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    for (int n = 0; n < cnt; n += 2) {
+      step(std::integral_constant<int, 0>{}, n);
+      if (n + 1 < cnt) step(std::integral_constant<int, 1>{}, n + 1);
     }
 
     // ---- normalise and store O (and LSE) for this lane's query ----
