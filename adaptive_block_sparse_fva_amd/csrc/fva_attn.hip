@@ -65,26 +65,30 @@ __device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)lds_base, 16, 0, 0);
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
-  constexpr int NW = BLK / 32;  // waves per workgroup
-  constexpr int KS = BLK / 32;  // 32-key sub-tiles of S^T
-  constexpr int DS = D / 16;    // k-steps of S^T = K Q^T
-  constexpr int DO = D / 32;    // 32-row sub-tiles of O^T
-  constexpr int PS = BLK / 16;  // k-steps of O^T += V^T P^T
-  constexpr int CH = D / 8;     // 16-byte chunks per K/V row
-  constexpr int RW = 64 / CH;   // rows written by one wave-wide LDS-DMA load
-  constexpr int NI = 32 / RW;   // LDS-DMA loads per wave per tile (a wave stages 32 rows)
-  constexpr int TILE = BLK * D; // elements of one K or V tile
-  static_assert(NW * 32 == BLK, "one wave per 32 rows");
+// One workgroup = one (head, query block) tile at a time; KB = keys per
+// sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks).
+template <int D, int BLK, int KB>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sparse_attn_fwd_kernel(AttnArgs a) {
+  constexpr int NW = BLK / 32;   // waves per workgroup (32 query rows each)
+  constexpr int SUB = BLK / KB;  // sub-blocks per kept key block
+  constexpr int KS = KB / 32;    // 32-key sub-tiles of S^T per sub-block
+  constexpr int DS = D / 16;     // k-steps of S^T = K Q^T
+  constexpr int DO = D / 32;     // 32-row sub-tiles of O^T
+  constexpr int PS = KB / 16;    // k-steps of O^T += V^T P^T
+  constexpr int CH = D / 8;      // 16-byte chunks per K/V row
+  constexpr int RW = 64 / CH;    // rows written by one wave-wide LDS-DMA load
+  constexpr int RPW = KB / NW;   // rows each wave stages per sub-block
+  constexpr int NI = RPW / RW;   // LDS-DMA loads per wave per tensor
+  constexpr int TILE = KB * D;   // elements of one K or V sub-tile
+  static_assert(NW * 32 == BLK && SUB * KB == BLK && NI >= 1 && NI * RW == RPW, "tiling");
 
-  // K and V tiles, rows of D elements, 16-byte chunk c of row r stored at
+  // K and V sub-tiles, rows of D elements, 16-byte chunk c of row r stored at
   // chunk position c ^ (r % CH): the 32 rows an MFMA operand read touches at
   // one logical chunk then fall into distinct banks.  Two buffers (0 and 1):
-  // the next key block streams in while the current one is used.  They are
-  // separate LDS objects and the block loop is unrolled by two, so the
-  // compiler can tell that loads into one buffer never alias reads of the
-  // other and does not wait for them.
+  // the next sub-block streams in while the current one is used.  They are
+  // separate LDS objects and the loop is unrolled by two, so the compiler can
+  // tell that loads into one buffer never alias reads of the other.
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[TILE];
@@ -96,9 +100,8 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int g16 = lane >> 4, s16 = lane & 15;
-  // staging role of this lane in a wave-wide LDS-DMA load
-  const int st_sub = lane / CH;          // row inside the load's RW rows
-  const int st_phys = lane % CH;         // chunk position it writes
+  const int st_sub = lane / CH;   // row inside one LDS-DMA load's RW rows
+  const int st_phys = lane % CH;  // chunk position this lane writes
 
   for (;;) {
     if (tid == 0) s_tile = (int)atomicAdd(&a.tile_counter[0], 1u);
@@ -134,48 +137,49 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int c0 = a.row_ptr[t], cnt = a.row_ptr[t + 1] - c0;
+    const int c0 = a.row_ptr[t];
+    const int nsub = (a.row_ptr[t + 1] - c0) * SUB;
     const int32_t* cols = a.col_idx + c0;
+    // first sequence position of sub-block u
+    auto sub_pos = [&](int u) { return cols[u / SUB] * BLK + (u % SUB) * KB; };
 
-    // Token index of each row this lane stages, one key block ahead.
+    // Token index of each row this lane stages, one sub-block ahead.
     // Positions past the end of the sequence (order = -1, last block only)
     // stage token 0 instead: their keys are masked to -inf before the
     // softmax, so their V rows are multiplied by exactly zero.
     int toks[NI];
-    auto load_toks = [&](int j) {
+    auto load_toks = [&](int pos) {
 #pragma unroll
-      for (int m = 0; m < NI; ++m)
-        toks[m] = max(a.order[j * BLK + wave * 32 + m * RW + st_sub], 0);
+      for (int m = 0; m < NI; ++m) toks[m] = max(a.order[pos + wave * RPW + m * RW + st_sub], 0);
     };
     auto issue = [&](bf16_t* kt, bf16_t* vt) {
-      kt += (wave * 32) * D;
-      vt += (wave * 32) * D;
+      kt += (wave * RPW) * D;
+      vt += (wave * RPW) * D;
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const int row = wave * 32 + m * RW + st_sub;
+        const int row = wave * RPW + m * RW + st_sub;
         const int64_t off = (int64_t)toks[m] * a.stride_token + ((st_phys ^ (row & (CH - 1))) * 8);
         lds_dma16(kh + off, kt + m * RW * D);
         lds_dma16(vh + off, vt + m * RW * D);
       }
     };
 
-    load_toks(cols[0]);
+    load_toks(sub_pos(0));
     issue(k_lds0, v_lds0);
-    if (cnt > 1) load_toks(cols[1]);
+    if (nsub > 1) load_toks(sub_pos(1));
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // one key block: compute on buffer CUR while the next block streams into
-    // the other buffer
-    auto step = [&](auto cur_tag, int n) {
+    // one sub-block: compute on buffer CUR while the next streams into the other
+    auto step = [&](auto cur_tag, int u) {
       constexpr int CUR = decltype(cur_tag)::value;
       const bf16_t* ks = CUR ? k_lds1 : k_lds0;
       const bf16_t* vs = CUR ? v_lds1 : v_lds0;
-      const int j = cols[n];
-      if (n + 1 < cnt) {
+      const int pos = sub_pos(u);
+      if (u + 1 < nsub) {
         if (CUR) issue(k_lds0, v_lds0);
         else issue(k_lds1, v_lds1);
-        if (n + 2 < cnt) load_toks(cols[n + 2]);
+        if (u + 2 < nsub) load_toks(sub_pos(u + 2));
       }
 
       // ---- S^T = K Q^T for this wave's 32 queries ----
@@ -193,11 +197,11 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
                                                           0, 0, 0);
         }
       }
-      // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of block j
+      // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
 
       // keys past the end of the sequence (only in the last block) get -inf
-      const int valid = min(BLK, a.n - j * BLK);
-      if (valid < BLK) {
+      const int valid = a.n - pos;
+      if (valid < KB) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -205,9 +209,9 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
             if (kk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) >= valid) s[kk][r] = -INFINITY;
       }
 
-  // ---- online softmax (base 2), row statistics per lane ----
-      // The running maximum m_run is only raised when a block's maximum
-      // exceeds it by more than 8 (a factor 2^8), so most blocks skip the
+      // ---- online softmax (base 2), row statistics per lane ----
+      // The running maximum m_run is only raised when a sub-block's maximum
+      // exceeds it by more than 8 (a factor 2^8), so most sub-blocks skip the
       // rescale of the accumulators; weights then stay below 2^8, and the
       // final division by the matching denominator makes the result exact.
       float mx = -INFINITY;
@@ -260,14 +264,14 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
         }
       }
 
-      // the next block's LDS-DMA loads (and token loads) have landed for every
-      // wave, and every wave is done reading this block's buffer
+      // the next sub-block's LDS-DMA loads (and token loads) have landed for
+      // every wave, and every wave is done reading this buffer
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     };
-    for (int n = 0; n < cnt; n += 2) {
-      step(std::integral_constant<int, 0>{}, n);
-      if (n + 1 < cnt) step(std::integral_constant<int, 1>{}, n + 1);
+    for (int u = 0; u < nsub; u += 2) {
+      step(std::integral_constant<int, 0>{}, u);
+      if (u + 1 < nsub) step(std::integral_constant<int, 1>{}, u + 1);
     }
 
     // ---- normalise and store O (and LSE) for this lane's query ----
@@ -299,15 +303,17 @@ __global__ __launch_bounds__(BLK * 2) void sparse_attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+constexpr int KEYS_PER_STEP = 64;
+
 template <int D, int BLK>
 static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
-  sparse_attn_fwd_kernel<D, BLK><<<grid, BLK * 2, 0, stream>>>(args);
+  sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP><<<grid, BLK * 2, 0, stream>>>(args);
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
 template <int D, int BLK>
 static int occupancy_t(int* blocks) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK>,
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP>,
                                                            BLK * 2, 0);
 }
 
