@@ -25,6 +25,13 @@
 //     double-buffered LDS tile while the current block is computed.
 #include <type_traits>
 
+#ifndef FVA_KB
+#define FVA_KB 64
+#endif
+#ifndef FVA_NBUF
+#define FVA_NBUF 2
+#endif
+
 #include "fva_common.h"
 
 namespace fva {
@@ -59,15 +66,36 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding and leaves the other counters alone (GFX9 encoding).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
 // lds_base + 16*l (lds_base must be the same for the whole wave).
 __device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Chunk swizzle of the K/V LDS tiles: logical 16-byte chunk c of row r is
+// stored at position c ^ swz(r).  For 16 chunks per row swz swaps the two
+// 2-bit halves of r mod 16: it is a bijection on any 16 consecutive rows
+// (K operand reads: 32 rows at one logical chunk), and the 8 rows x 4 chunks
+// that one transposing V read covers land on all 16 positions exactly twice.
+// For 8 chunks per row (d = 64) rows alternate between the two bank halves,
+// so swz uses r / 2.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
 // One workgroup = one (head, query block) tile at a time; KB = keys per
-// sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks).
-template <int D, int BLK, int KB>
+// sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks,
+// numbered u = 0 .. nsub-1 along the tile's kept list).  K/V sub-tiles stream
+// through a ring of NBUF LDS slots: sub-block u+NBUF-1 is issued while u is
+// computed, and the token indices that address it are fetched two steps
+// before that.
+template <int D, int BLK, int KB, int NBUF>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = BLK / 32;   // waves per workgroup (32 query rows each)
@@ -82,18 +110,36 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int NI = RPW / RW;   // LDS-DMA loads per wave per tensor
   constexpr int TILE = KB * D;   // elements of one K or V sub-tile
   static_assert(NW * 32 == BLK && SUB * KB == BLK && NI >= 1 && NI * RW == RPW, "tiling");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring slots");
 
   // K and V sub-tiles, rows of D elements, 16-byte chunk c of row r stored at
-  // chunk position c ^ (r % CH): the 32 rows an MFMA operand read touches at
-  // one logical chunk then fall into distinct banks.  Two buffers (0 and 1):
-  // the next sub-block streams in while the current one is used.  They are
-  // separate LDS objects and the loop is unrolled by two, so the compiler can
-  // tell that loads into one buffer never alias reads of the other.
+  // chunk position c ^ swz(r) (see swz).  The ring slots are separate LDS
+  // objects and the loop is unrolled by NBUF, so the compiler can tell that
+  // loads into one slot never alias reads of another and does not wait for
+  // them.
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds2[NBUF > 2 ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds2[NBUF > 2 ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds3[NBUF > 3 ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds3[NBUF > 3 ? TILE : 8];
   __shared__ int s_tile;
+  auto kslot = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    if constexpr (B == 0) return k_lds0;
+    else if constexpr (B == 1) return k_lds1;
+    else if constexpr (B == 2) return k_lds2;
+    else return k_lds3;
+  };
+  auto vslot = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    if constexpr (B == 0) return v_lds0;
+    else if constexpr (B == 1) return v_lds1;
+    else if constexpr (B == 2) return v_lds2;
+    else return v_lds3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,71 +183,116 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
+    // Per-lane LDS operand offsets (elements).  The swizzle depends on the row
+    // modulo 16 only, which is the same for every 32-key sub-tile (K) and
+    // every 16-key k-step (V), so sub-tiles and k-steps differ by constants.
+    int koff[DS];
+#pragma unroll
+    for (int d = 0; d < DS; ++d) koff[d] = l32 * D + ((2 * d + hf) ^ swz<CH>(l32)) * 8;
+    int voff[DO][2];
+    {
+      const int vr = 4 * (g16 >> 1) + (s16 >> 2);
+#pragma unroll
+      for (int d = 0; d < DO; ++d) {
+        const int c = d * 4 + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+        voff[d][0] = vr * D + (c ^ swz<CH>(vr)) * 8 + 4 * (s16 & 1);
+        voff[d][1] = (vr + 8) * D + (c ^ swz<CH>(vr + 8)) * 8 + 4 * (s16 & 1);
+      }
+    }
+
     const int c0 = a.row_ptr[t];
     const int nsub = (a.row_ptr[t + 1] - c0) * SUB;
     const int32_t* cols = a.col_idx + c0;
     // first sequence position of sub-block u
     auto sub_pos = [&](int u) { return cols[u / SUB] * BLK + (u % SUB) * KB; };
 
-    // Token index of each row this lane stages, one sub-block ahead.
-    // Positions past the end of the sequence (order = -1, last block only)
-    // stage token 0 instead: their keys are masked to -inf before the
-    // softmax, so their V rows are multiplied by exactly zero.
-    int toks[NI];
-    auto load_toks = [&](int pos) {
+    // Token index of each row this lane stages.  Positions past the end of
+    // the sequence (order = -1, last block only) stage token 0 instead: their
+    // keys are masked to -inf before the softmax, so their V rows are
+    // multiplied by exactly zero.
+    auto load_toks = [&](int u, int (&tk)[NI]) {
+      const int pos = sub_pos(u);
 #pragma unroll
-      for (int m = 0; m < NI; ++m) toks[m] = max(a.order[pos + wave * RPW + m * RW + st_sub], 0);
+      for (int m = 0; m < NI; ++m) tk[m] = max(a.order[pos + wave * RPW + m * RW + st_sub], 0);
     };
-    auto issue = [&](bf16_t* kt, bf16_t* vt) {
+    auto issue = [&](bf16_t* kt, bf16_t* vt, const int (&tk)[NI]) {
       kt += (wave * RPW) * D;
       vt += (wave * RPW) * D;
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
         const int row = wave * RPW + m * RW + st_sub;
-        const int64_t off = (int64_t)toks[m] * a.stride_token + ((st_phys ^ (row & (CH - 1))) * 8);
+        const int64_t off = (int64_t)tk[m] * a.stride_token + ((st_phys ^ swz<CH>(row)) * 8);
         lds_dma16(kh + off, kt + m * RW * D);
         lds_dma16(vh + off, vt + m * RW * D);
       }
     };
 
-    load_toks(sub_pos(0));
-    issue(k_lds0, v_lds0);
-    if (nsub > 1) load_toks(sub_pos(1));
+    // Prologue: sub-blocks 0 .. NBUF-2 in flight, tokens of NBUF-1 and NBUF
+    // in hand.  In the loop a step issues, in this order, the token loads for
+    // sub-block u+NBUF+1 and the LDS-DMA loads of u+NBUF-1; waiting for a
+    // token load therefore never waits for a DMA that is still needed later.
+    int tk_a[NI], tk_b[NI];
+    {
+      int tk[NI];
+      load_toks(0, tk);
+      issue(k_lds0, v_lds0, tk);
+      if constexpr (NBUF > 2) {
+        if (nsub > 1) { load_toks(1, tk); issue(k_lds1, v_lds1, tk); }
+      }
+      if constexpr (NBUF > 3) {
+        if (nsub > 2) { load_toks(2, tk); issue(k_lds2, v_lds2, tk); }
+      }
+      if (nsub > NBUF - 1) load_toks(NBUF - 1, tk_a);
+      if (nsub > NBUF) load_toks(NBUF, tk_b);
+    }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // one sub-block: compute on buffer CUR while the next streams into the other
+    // one sub-block: compute on slot CUR while later sub-blocks stream in
     auto step = [&](auto cur_tag, int u) {
       constexpr int CUR = decltype(cur_tag)::value;
-      const bf16_t* ks = CUR ? k_lds1 : k_lds0;
-      const bf16_t* vs = CUR ? v_lds1 : v_lds0;
+      constexpr int NXT = (CUR + NBUF - 1) % NBUF;
+      const bf16_t* ks = kslot(std::integral_constant<int, CUR>{});
+      const bf16_t* vs = vslot(std::integral_constant<int, CUR>{});
       const int pos = sub_pos(u);
-      if (u + 1 < nsub) {
-        if (CUR) issue(k_lds0, v_lds0);
-        else issue(k_lds1, v_lds1);
-        if (u + 2 < nsub) load_toks(sub_pos(u + 2));
+      int tk_c[NI] = {};
+      if (u + NBUF + 1 < nsub) load_toks(u + NBUF + 1, tk_c);
+      if (u + NBUF - 1 < nsub)
+        issue(kslot(std::integral_constant<int, NXT>{}), vslot(std::integral_constant<int, NXT>{}), tk_a);
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        tk_a[m] = tk_b[m];
+        tk_b[m] = tk_c[m];
       }
 
       // ---- S^T = K Q^T for this wave's 32 queries ----
+      // The DS operand reads of a 32-key sub-tile are all issued before its
+      // MFMAs (the scheduling groups below keep them together), so LDS latency
+      // is paid once per sub-tile rather than once per MFMA.
       f32x16 s[KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
+        u32x4 kf[DS];
+#pragma unroll
+        for (int d = 0; d < DS; ++d)
+          kf[d] = *reinterpret_cast<const u32x4*>(&ks[kk * 32 * D + koff[d]]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
-        const int row = kk * 32 + l32;
 #pragma unroll
-        for (int d = 0; d < DS; ++d) {
-          const int phys = (2 * d + hf) ^ (row & (CH - 1));
-          const u32x4 w = *reinterpret_cast<const u32x4*>(&ks[row * D + phys * 8]);
-          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[d], s[kk],
+        for (int d = 0; d < DS; ++d)
+          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[d]), qf[d], s[kk],
                                                           0, 0, 0);
-        }
+        __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, DS, 0);
       }
       // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
 
       // keys past the end of the sequence (only in the last block) get -inf
+      // (a real branch: the empty asm keeps the compiler from turning it
+      // into selects that would run on every sub-block)
       const int valid = a.n - pos;
-      if (valid < KB) {
+      if (__builtin_expect(valid < KB, 0)) {
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -248,30 +339,38 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       // d*4 + 2*(g16%2) + (s16%4)/2
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
+        u32x4 vf[DO];
+#pragma unroll
+        for (int d = 0; d < DO; ++d) {
+          const u32x2 lo = lds_read_tr16(&vs[ps * 16 * D + voff[d][0]]);
+          const u32x2 hi = lds_read_tr16(&vs[ps * 16 * D + voff[d][1]]);
+          vf[d] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[ps >> 1][(ps & 1) * 8 + e];
-        const int vr0 = ps * 16 + 4 * (g16 >> 1) + (s16 >> 2);
-        const int vr1 = vr0 + 8;
 #pragma unroll
-        for (int d = 0; d < DO; ++d) {
-          const int c = d * 4 + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-          const u32x2 lo = lds_read_tr16(&vs[vr0 * D + ((c ^ (vr0 & (CH - 1))) * 8) + 4 * (s16 & 1)]);
-          const u32x2 hi = lds_read_tr16(&vs[vr1 * D + ((c ^ (vr1 & (CH - 1))) * 8) + 4 * (s16 & 1)]);
-          const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf, acc_o[d],
+        for (int d = 0; d < DO; ++d)
+          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[d]), pf, acc_o[d],
                                                              0, 0, 0);
-        }
       }
 
-      // the next sub-block's LDS-DMA loads (and token loads) have landed for
-      // every wave, and every wave is done reading this buffer
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // Sub-block u+1 has landed for every wave and every wave is done with
+      // slot CUR.  In steady state the loads issued in the last NBUF-2 steps
+      // (3*NI per step) may stay in flight; near the end wait for everything.
+      if (u + NBUF + 1 < nsub) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * 3 * NI));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
     };
-    for (int u = 0; u < nsub; u += 2) {
+    for (int u = 0; u < nsub; u += NBUF) {
       step(std::integral_constant<int, 0>{}, u);
       if (u + 1 < nsub) step(std::integral_constant<int, 1>{}, u + 1);
+      if constexpr (NBUF > 2) {
+        if (u + 2 < nsub) step(std::integral_constant<int, 2 % NBUF>{}, u + 2);
+      }
+      if constexpr (NBUF > 3) {
+        if (u + 3 < nsub) step(std::integral_constant<int, 3 % NBUF>{}, u + 3);
+      }
     }
 
     // ---- normalise and store O (and LSE) for this lane's query ----
@@ -303,17 +402,18 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-constexpr int KEYS_PER_STEP = 64;
+constexpr int KEYS_PER_STEP = FVA_KB;
+constexpr int RING_SLOTS = FVA_NBUF;
 
 template <int D, int BLK>
 static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
-  sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP><<<grid, BLK * 2, 0, stream>>>(args);
+  sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS><<<grid, BLK * 2, 0, stream>>>(args);
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
 template <int D, int BLK>
 static int occupancy_t(int* blocks) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP>,
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS>,
                                                            BLK * 2, 0);
 }
 
