@@ -51,6 +51,23 @@ def kept_flops_and_pairs(row_ptr, col_idx, n_tokens, block, head_dim, num_heads,
     return int(4 * head_dim * int((q_sizes * per_row).sum())), int(len(col_idx))
 
 
+def measured_traffic():
+    """HBM traffic of the attention launch from the committed counter summary,
+    or None when the kernel source differs from the one the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "sparse_attn_fwd_rank480p_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] * 1024
+               + rec["write_kib_per_dispatch"] * rec["write_scale"] * 1024)
+
+
 def list_schedule_makespan(costs, workers):
     """Greedy list scheduling (each tile to the earliest-free worker)."""
     import heapq
@@ -245,8 +262,9 @@ def main():
                       "frac": round(route_gbs / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "sparse_attn_fwd_kernel<128,128>",
+                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if wl.name == "rank480p" else None,
+                     "kernel": "sparse_attn_fwd_kernel<128,128,64,2>",
                      "algorithmic_flops_per_launch": kept},
         "cu_imbalance": {"workgroups": workers, "lpt": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4)},
