@@ -126,6 +126,9 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds3[NBUF > 3 ? TILE : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds3[NBUF > 3 ? TILE : 8];
   __shared__ int s_tile;
+  // the tile's kept key-block list, staged once per tile so that the per-step
+  // position lookups are LDS broadcasts rather than global loads
+  __shared__ int s_cols[FVA_MAX_BLOCKS];
   auto kslot = [&](auto b) -> bf16_t* {
     constexpr int B = decltype(b)::value;
     if constexpr (B == 0) return k_lds0;
@@ -201,10 +204,12 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
     }
 
     const int c0 = a.row_ptr[t];
-    const int nsub = (a.row_ptr[t + 1] - c0) * SUB;
-    const int32_t* cols = a.col_idx + c0;
+    const int ncols = a.row_ptr[t + 1] - c0;
+    const int nsub = ncols * SUB;
+    for (int c = tid; c < ncols; c += BLK * 2) s_cols[c] = a.col_idx[c0 + c];
+    __syncthreads();
     // first sequence position of sub-block u
-    auto sub_pos = [&](int u) { return cols[u / SUB] * BLK + (u % SUB) * KB; };
+    auto sub_pos = [&](int u) { return s_cols[u / SUB] * BLK + (u % SUB) * KB; };
 
     // Token index of each row this lane stages.  Positions past the end of
     // the sequence (order = -1, last block only) stage token 0 instead: their
@@ -270,6 +275,10 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       // MFMAs (the scheduling groups below keep them together), so LDS latency
       // is paid once per sub-tile rather than once per MFMA.
       f32x16 s[KS];
+      // matrix phases run at raised wave priority: the SIMD then issues this
+      // wave's MFMAs as soon as they are ready and fills the gaps with the
+      // other resident wave's softmax work
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         u32x4 kf[DS];
@@ -285,6 +294,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, DS, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
 
       // keys past the end of the sequence (only in the last block) get -inf
@@ -337,6 +347,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       // ps*16 + 4*(g16/2) + s16/4 (and +8), features
       // d*32 + 16*(g16%2) + 4*(s16%4), i.e. half (s16&1) of logical chunk
       // d*4 + 2*(g16%2) + (s16%4)/2
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
         u32x4 vf[DO];
@@ -354,6 +365,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
           acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[d]), pf, acc_o[d],
                                                              0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
 
       // Sub-block u+1 has landed for every wave and every wave is done with
       // slot CUR.  In steady state the loads issued in the last NBUF-2 steps
