@@ -279,20 +279,29 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       // wave's MFMAs as soon as they are ready and fills the gaps with the
       // other resident wave's softmax work
       __builtin_amdgcn_s_setprio(1);
+      // The KS accumulation chains are interleaved (a dependent MFMA chain
+      // issues about a third slower than two independent ones), and the DS
+      // operand reads run two k-steps ahead of the MFMAs that use them.
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        u32x4 kf[DS];
-#pragma unroll
-        for (int d = 0; d < DS; ++d)
-          kf[d] = *reinterpret_cast<const u32x4*>(&ks[kk * 32 * D + koff[d]]);
+      for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
 #pragma unroll
-        for (int d = 0; d < DS; ++d)
-          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[d]), qf[d], s[kk],
+      for (int d = 0; d < DS; ++d) {
+        u32x4 kf[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          kf[kk] = *reinterpret_cast<const u32x4*>(&ks[kk * 32 * D + koff[d]]);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qf[d], s[kk],
                                                           0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, DS, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+#pragma unroll
+      for (int d = 0; d < DS; ++d) {
+        __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+        if (d + 2 < DS) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
       }
       __builtin_amdgcn_s_setprio(0);
       // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
