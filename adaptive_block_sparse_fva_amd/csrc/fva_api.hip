@@ -9,18 +9,18 @@
 
 namespace fva {
 
-int launch_route(const fva_problem& p, int nb, const void* q, const void* k,
+int launch_route(const fva_problem& p, int nb, const void* q, const void* k, const void* v,
                  float* scores, int16_t* ranked, int32_t* row_count,
-                 int32_t* head_count, int32_t* order, float* qbar, float* kbar,
+                 int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
                  float sm_scale, hipStream_t stream);
 int launch_plan(const fva_problem& p, int nb, const int16_t* ranked,
                 const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
                 int32_t* head_count_final, int32_t* tile_order,
                 uint32_t* tile_counter, hipStream_t stream);
-int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* k,
-                const void* v, const int32_t* order, const int32_t* row_ptr,
-                const int32_t* col_idx, const int32_t* tile_order, uint32_t* tile_counter,
-                void* o, float* lse, float sm_scale, hipStream_t stream);
+int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
+                const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
+                const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
+                float sm_scale, hipStream_t stream);
 int attn_blocks_per_cu(int d, int block);
 
 static thread_local char g_last_error[256] = "";
@@ -101,6 +101,11 @@ static int64_t workspace_need(const fva_problem* p, int nb) {
   return 2 * (int64_t)p->num_heads * nb * p->head_dim * (int64_t)sizeof(float);
 }
 
+// K and V of every head re-laid out in position order: 2 x H x nb*B x d bf16.
+static int64_t kv_elems(const fva_problem* p, int nb) {
+  return 2 * (int64_t)p->num_heads * nb * p->block * p->head_dim;
+}
+
 static float effective_scale(const fva_problem* p) {
   return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
 }
@@ -140,6 +145,7 @@ int fva_sizes(const fva_problem* prob, fva_sizes_t* out) {
   out->col_idx_capacity = rows * nb;
   out->workspace_bytes = workspace_need(prob, nb);
   out->tile_counter_elems = 2;
+  out->kv_elems = kv_elems(prob, nb);
   return FVA_OK;
 }
 
@@ -155,20 +161,22 @@ int fva_attn_workgroups(const fva_problem* prob, int32_t* out) {
   return FVA_OK;
 }
 
-int fva_route(const fva_problem* prob, const void* q, const void* k, float* scores,
-              int16_t* ranked, int32_t* row_count, int32_t* head_count, int32_t* order,
-              void* workspace, size_t workspace_bytes, void* stream) {
+int fva_route(const fva_problem* prob, const void* q, const void* k, const void* v,
+              float* scores, int16_t* ranked, int32_t* row_count, int32_t* head_count,
+              int32_t* order, void* kv, void* workspace, size_t workspace_bytes, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
-  if (!q || !k || !scores || !ranked || !row_count || !head_count || !order || !workspace)
+  if (!q || !k || !v || !scores || !ranked || !row_count || !head_count || !order || !kv ||
+      !workspace)
     return FVA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(workspace)) return FVA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kv) || !aligned16(workspace))
+    return FVA_ERR_ARG;
   if ((int64_t)workspace_bytes < workspace_need(prob, nb)) return FVA_ERR_WORKSPACE;
   float* qbar = (float*)workspace;
   float* kbar = qbar + (int64_t)prob->num_heads * nb * prob->head_dim;
-  return launch_route(*prob, nb, q, k, scores, ranked, row_count, head_count, order, qbar, kbar,
-                      effective_scale(prob), (hipStream_t)stream);
+  return launch_route(*prob, nb, q, k, v, scores, ranked, row_count, head_count, order, kv, qbar,
+                      kbar, effective_scale(prob), (hipStream_t)stream);
 }
 
 int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_count,
@@ -184,22 +192,21 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_
                      tile_order, tile_counter, (hipStream_t)stream);
 }
 
-int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* k, const void* v,
+int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                         const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
                         void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
-  if (!q || !k || !v || !order || !row_ptr || !col_idx || !tile_order || !tile_counter || !o)
+  if (!q || !kv || !order || !row_ptr || !col_idx || !tile_order || !tile_counter || !o)
     return FVA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(order))
-    return FVA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned16(order)) return FVA_ERR_ARG;
   int grid = 0;
   st = attn_grid(*prob, nb, &grid);
   if (st) return st;
-  return launch_attn(*prob, nb, grid, q, k, v, order, row_ptr, col_idx, tile_order,
-                     tile_counter, o, lse, effective_scale(prob), (hipStream_t)stream);
+  return launch_attn(*prob, nb, grid, q, kv, order, row_ptr, col_idx, tile_order, tile_counter,
+                     o, lse, effective_scale(prob), (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -20,9 +20,13 @@
 //     straight from the S^T accumulators; the key permutation implied by the
 //     accumulator layout is applied to the V^T reads, so no register shuffles
 //     are needed;
-//   - K and V rows are gathered through the order table (position -> token)
-//     into registers one block ahead and written to the other half of a
-//     double-buffered LDS tile while the current block is computed.
+//   - K and V come re-laid out in the video-aware order by the routing pass
+//     (K row-major per position, V transposed per 64-position sub-block with
+//     its columns in the order the S^T accumulators hold their keys), so the
+//     kernel streams contiguous sub-tiles into a ring of LDS slots with
+//     direct buffer -> LDS loads whose addresses are per-lane constants plus
+//     one scalar offset, and reads its V^T operands with plain 16-byte LDS
+//     loads.
 #include <type_traits>
 
 #ifndef FVA_KB
@@ -38,8 +42,8 @@ namespace fva {
 
 struct AttnArgs {
   const bf16_t* q;
-  const bf16_t* k;
-  const bf16_t* v;
+  const bf16_t* kp;  // [H][npad][d], K in position order (zero rows past N)
+  const bf16_t* vt;  // [H][npad/64][d][64], V^T per 64-position sub-block
   bf16_t* o;
   float* lse;
   const int32_t* order;
@@ -49,19 +53,14 @@ struct AttnArgs {
   uint32_t* tile_counter;
   int64_t stride_head, stride_token;
   int n, nb, num_tiles;
+  int npad;          // nb * B
   float scale_log2;  // sm_scale * log2(e)
 };
 
-typedef __attribute__((address_space(3))) __bf16 lds_bf16;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
-// source lane s fetches the 4 bf16 at its own address; destination lane i then
-// holds element i%4 of the chunks fetched by lanes i/4, i/4+4, i/4+8, i/4+12.
-__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
+// Buffer resource over one head's rows of the re-laid-out K or V: raw byte
+// addressing, num_records = bytes (loads beyond return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -70,19 +69,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 // outstanding and leaves the other counters alone (GFX9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base must be the same for the whole wave).
-__device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)lds_base, 16, 0, 0);
+// Direct buffer -> LDS load of 16 bytes per lane from byte offset
+// voff + soff: lane l's bytes land at lds_base + 16*l (lds_base and soff
+// wave-uniform).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, bf16_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, soff, 0, 0);
 }
 
-// Chunk swizzle of the K/V LDS tiles: logical 16-byte chunk c of row r is
-// stored at position c ^ swz(r).  For 16 chunks per row swz swaps the two
-// 2-bit halves of r mod 16: it is a bijection on any 16 consecutive rows
-// (K operand reads: 32 rows at one logical chunk), and the 8 rows x 4 chunks
-// that one transposing V read covers land on all 16 positions exactly twice.
-// For 8 chunks per row (d = 64) rows alternate between the two bank halves,
-// so swz uses r / 2.
+// Chunk swizzle of the LDS tiles: logical 16-byte chunk c of row r is stored
+// at position c ^ swz(r).  For 16 chunks per row (K, d = 128) swz swaps the
+// two 2-bit halves of r mod 16, a bijection on any 16 consecutive rows (the
+// K operand reads 32 rows at one logical chunk).  For 8 chunks per row (K at
+// d = 64, and every V^T tile: 64 keys per row) rows alternate between the two
+// bank halves, so swz uses r / 2.
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -91,10 +90,9 @@ __device__ __forceinline__ int swz(int r) {
 
 // One workgroup = one (head, query block) tile at a time; KB = keys per
 // sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks,
-// numbered u = 0 .. nsub-1 along the tile's kept list).  K/V sub-tiles stream
-// through a ring of NBUF LDS slots: sub-block u+NBUF-1 is issued while u is
-// computed, and the token indices that address it are fetched two steps
-// before that.
+// numbered u = 0 .. nsub-1 along the tile's kept list).  K and V^T sub-tiles
+// stream through a ring of NBUF LDS slots: sub-block u+NBUF-1 is issued while
+// u is computed.
 template <int D, int BLK, int KB, int NBUF>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_attn_fwd_kernel(AttnArgs a) {
@@ -105,15 +103,20 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int DO = D / 32;     // 32-row sub-tiles of O^T
   constexpr int PS = KB / 16;    // k-steps of O^T += V^T P^T
   constexpr int CH = D / 8;      // 16-byte chunks per K/V row
-  constexpr int RW = 64 / CH;    // rows written by one wave-wide LDS-DMA load
-  constexpr int RPW = KB / NW;   // rows each wave stages per sub-block
-  constexpr int NI = RPW / RW;   // LDS-DMA loads per wave per tensor
-  constexpr int TILE = KB * D;   // elements of one K or V sub-tile
+  constexpr int RW = 64 / CH;    // K rows written by one wave-wide LDS-DMA load
+  constexpr int RPW = KB / NW;   // K rows each wave stages per sub-block
+  constexpr int NI = RPW / RW;   // K LDS-DMA loads per wave per sub-block
+  constexpr int VCH = KB / 8;    // 16-byte chunks per V^T row
+  constexpr int VRW = 64 / VCH;  // V^T rows written by one LDS-DMA load
+  constexpr int VRPW = D / NW;   // V^T rows each wave stages
+  constexpr int NIV = VRPW / VRW;  // V^T LDS-DMA loads per wave per sub-block
+  constexpr int TILE = KB * D;   // elements of one K or V^T sub-tile
   static_assert(NW * 32 == BLK && SUB * KB == BLK && NI >= 1 && NI * RW == RPW, "tiling");
+  static_assert(KB == 64 && NIV >= 1 && NIV * VRW == VRPW, "V^T tiling (64-key sub-blocks)");
   static_assert(NBUF >= 2 && NBUF <= 4, "ring slots");
 
-  // K and V sub-tiles, rows of D elements, 16-byte chunk c of row r stored at
-  // chunk position c ^ swz(r) (see swz).  The ring slots are separate LDS
+  // K sub-tiles: KB rows (keys) of D elements; V^T sub-tiles: D rows of KB
+  // keys; 16-byte chunk c of row r stored at position c ^ swz(r).  The ring slots are separate LDS
   // objects and the loop is unrolled by NBUF, so the compiler can tell that
   // loads into one slot never alias reads of another and does not wait for
   // them.
@@ -148,9 +151,20 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int g16 = lane >> 4, s16 = lane & 15;
-  const int st_sub = lane / CH;   // row inside one LDS-DMA load's RW rows
-  const int st_phys = lane % CH;  // chunk position this lane writes
+  // LDS-DMA: byte offset (inside one sub-block's contiguous K or V^T
+  // sub-tile) of the logical chunk that lands at this lane's position
+  uint32_t kdma[NI], vdma[NIV];
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int row = wave * RPW + m * RW + lane / CH;
+    kdma[m] = (uint32_t)(row * D + ((lane % CH) ^ swz<CH>(row)) * 8) * 2u;
+  }
+#pragma unroll
+  for (int m = 0; m < NIV; ++m) {
+    const int row = wave * VRPW + m * VRW + lane / VCH;
+    vdma[m] = (uint32_t)(row * KB + ((lane % VCH) ^ swz<VCH>(row)) * 8) * 2u;
+  }
+  const uint32_t head_bytes = (uint32_t)a.npad * D * 2u;
 
   for (;;) {
     if (tid == 0) s_tile = (int)atomicAdd(&a.tile_counter[0], 1u);
@@ -163,8 +177,9 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
     const int h = t / a.nb;
     const int i = t - h * a.nb;
     const int64_t hoff = (int64_t)h * a.stride_head;
-    const bf16_t* kh = a.k + hoff;
-    const bf16_t* vh = a.v + hoff;
+    const int64_t ph = (int64_t)h * a.npad * D;
+    const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.kp + ph, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.vt + ph, head_bytes);
 
     // Q fragments of this lane's query row (zeros past the end of the sequence)
     const int qtok = a.order[i * BLK + wave * 32 + l32];
@@ -192,16 +207,12 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
     int koff[DS];
 #pragma unroll
     for (int d = 0; d < DS; ++d) koff[d] = l32 * D + ((2 * d + hf) ^ swz<CH>(l32)) * 8;
-    int voff[DO][2];
-    {
-      const int vr = 4 * (g16 >> 1) + (s16 >> 2);
+    // V^T operand of k-step ps: row 32dt + l32, logical chunk 2ps + hf (its 8
+    // columns are the keys of this lane's P^T operand); the swizzle of rows
+    // 32dt + l32 does not depend on dt
+    int voff[PS];
 #pragma unroll
-      for (int d = 0; d < DO; ++d) {
-        const int c = d * 4 + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-        voff[d][0] = vr * D + (c ^ swz<CH>(vr)) * 8 + 4 * (s16 & 1);
-        voff[d][1] = (vr + 8) * D + (c ^ swz<CH>(vr + 8)) * 8 + 4 * (s16 & 1);
-      }
-    }
+    for (int ps = 0; ps < PS; ++ps) voff[ps] = l32 * KB + ((2 * ps + hf) ^ swz<VCH>(l32)) * 8;
 
     const int c0 = a.row_ptr[t];
     const int ncols = a.row_ptr[t + 1] - c0;
@@ -211,44 +222,23 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
     // first sequence position of sub-block u
     auto sub_pos = [&](int u) { return s_cols[u / SUB] * BLK + (u % SUB) * KB; };
 
-    // Token index of each row this lane stages.  Positions past the end of
-    // the sequence (order = -1, last block only) stage token 0 instead: their
-    // keys are masked to -inf before the softmax, so their V rows are
-    // multiplied by exactly zero.
-    auto load_toks = [&](int u, int (&tk)[NI]) {
-      const int pos = sub_pos(u);
+    // K and V^T sub-tiles of sub-block u: both start at byte pos * D * 2 of
+    // their head's re-laid-out buffer
+    auto issue = [&](bf16_t* kt, bf16_t* vt, int u) {
+      const int soff = __builtin_amdgcn_readfirstlane(sub_pos(u) * D * 2);
 #pragma unroll
-      for (int m = 0; m < NI; ++m) tk[m] = max(a.order[pos + wave * RPW + m * RW + st_sub], 0);
-    };
-    auto issue = [&](bf16_t* kt, bf16_t* vt, const int (&tk)[NI]) {
-      kt += (wave * RPW) * D;
-      vt += (wave * RPW) * D;
+      for (int m = 0; m < NI; ++m) lds_dma16(rk, kdma[m], soff, kt + (wave * RPW + m * RW) * D);
 #pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        const int row = wave * RPW + m * RW + st_sub;
-        const int64_t off = (int64_t)tk[m] * a.stride_token + ((st_phys ^ swz<CH>(row)) * 8);
-        lds_dma16(kh + off, kt + m * RW * D);
-        lds_dma16(vh + off, vt + m * RW * D);
-      }
+      for (int m = 0; m < NIV; ++m) lds_dma16(rv, vdma[m], soff, vt + (wave * VRPW + m * VRW) * KB);
     };
 
-    // Prologue: sub-blocks 0 .. NBUF-2 in flight, tokens of NBUF-1 and NBUF
-    // in hand.  In the loop a step issues, in this order, the token loads for
-    // sub-block u+NBUF+1 and the LDS-DMA loads of u+NBUF-1; waiting for a
-    // token load therefore never waits for a DMA that is still needed later.
-    int tk_a[NI], tk_b[NI];
-    {
-      int tk[NI];
-      load_toks(0, tk);
-      issue(k_lds0, v_lds0, tk);
-      if constexpr (NBUF > 2) {
-        if (nsub > 1) { load_toks(1, tk); issue(k_lds1, v_lds1, tk); }
-      }
-      if constexpr (NBUF > 3) {
-        if (nsub > 2) { load_toks(2, tk); issue(k_lds2, v_lds2, tk); }
-      }
-      if (nsub > NBUF - 1) load_toks(NBUF - 1, tk_a);
-      if (nsub > NBUF) load_toks(NBUF, tk_b);
+    // Prologue: sub-blocks 0 .. NBUF-2 in flight and landed.
+    issue(k_lds0, v_lds0, 0);
+    if constexpr (NBUF > 2) {
+      if (nsub > 1) issue(k_lds1, v_lds1, 1);
+    }
+    if constexpr (NBUF > 3) {
+      if (nsub > 2) issue(k_lds2, v_lds2, 2);
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -260,15 +250,8 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       const bf16_t* ks = kslot(std::integral_constant<int, CUR>{});
       const bf16_t* vs = vslot(std::integral_constant<int, CUR>{});
       const int pos = sub_pos(u);
-      int tk_c[NI] = {};
-      if (u + NBUF + 1 < nsub) load_toks(u + NBUF + 1, tk_c);
       if (u + NBUF - 1 < nsub)
-        issue(kslot(std::integral_constant<int, NXT>{}), vslot(std::integral_constant<int, NXT>{}), tk_a);
-#pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        tk_a[m] = tk_b[m];
-        tk_b[m] = tk_c[m];
-      }
+        issue(kslot(std::integral_constant<int, NXT>{}), vslot(std::integral_constant<int, NXT>{}), u + NBUF - 1);
 
       // ---- S^T = K Q^T for this wave's 32 queries ----
       // The DS operand reads of a 32-key sub-tile are all issued before its
@@ -351,21 +334,14 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
         }
       l_run += rs;
 
-      // ---- O^T += V^T P^T; V^T fragments come from row-major V by
-      // transposing reads: source lane s16 of lane group g16 fetches keys
-      // ps*16 + 4*(g16/2) + s16/4 (and +8), features
-      // d*32 + 16*(g16%2) + 4*(s16%4), i.e. half (s16&1) of logical chunk
-      // d*4 + 2*(g16%2) + (s16%4)/2
+      // ---- O^T += V^T P^T; the V^T operand of k-step ps and row tile d is
+      // one 16-byte LDS load ----
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
         u32x4 vf[DO];
 #pragma unroll
-        for (int d = 0; d < DO; ++d) {
-          const u32x2 lo = lds_read_tr16(&vs[ps * 16 * D + voff[d][0]]);
-          const u32x2 hi = lds_read_tr16(&vs[ps * 16 * D + voff[d][1]]);
-          vf[d] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+        for (int d = 0; d < DO; ++d) vf[d] = *reinterpret_cast<const u32x4*>(&vs[d * 32 * KB + voff[ps]]);
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[ps >> 1][(ps & 1) * 8 + e];
@@ -378,8 +354,8 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
 
       // Sub-block u+1 has landed for every wave and every wave is done with
       // slot CUR.  In steady state the loads issued in the last NBUF-2 steps
-      // (3*NI per step) may stay in flight; near the end wait for everything.
-      if (u + NBUF + 1 < nsub) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * 3 * NI));
+      // may stay in flight; near the end wait for everything.
+      if (u + NBUF < nsub) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * (NI + NIV)));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
     };
@@ -450,14 +426,18 @@ int attn_blocks_per_cu(int d, int block) {
   return b < 1 ? 1 : b;
 }
 
-int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* k,
-                const void* v, const int32_t* order, const int32_t* row_ptr,
-                const int32_t* col_idx, const int32_t* tile_order, uint32_t* tile_counter,
-                void* o, float* lse, float sm_scale, hipStream_t stream) {
+int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
+                const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
+                const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
+                float sm_scale, hipStream_t stream) {
+  const int npad = nb * p.block;
+  const bf16_t* kp = (const bf16_t*)kv;
+  const bf16_t* vt = kp + (int64_t)p.num_heads * npad * p.head_dim;
   AttnArgs a;
   a.q = (const bf16_t*)q;
-  a.k = (const bf16_t*)k;
-  a.v = (const bf16_t*)v;
+  a.kp = kp;
+  a.vt = vt;
+  a.npad = npad;
   a.o = (bf16_t*)o;
   a.lse = lse;
   a.order = order;

@@ -104,6 +104,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Layout of the re-laid-out K and V (written by the routing pass, read by the
+// attention kernel), per head h with npad = nb*B positions:
+//   kp[h][p][c]        = K[token order[p]][c]        (zero rows past N)
+//   vt[h][s][c][j]     = V[token order[64 s + vt_key(j)]][c]
+// V is transposed per 64-position sub-block s.  Column j holds key position
+// vt_key(j) of the sub-block: the order in which the S^T accumulators of the
+// attention kernel hold their keys (register r of a 32-key sub-tile,
+// half-wave hf: key 8(r/4) + 4hf + r%4), so that 8 consecutive columns are
+// exactly the keys of one lane's P^T operand and the V^T operand is one
+// 16-byte LDS load.
+constexpr int VT_KEYS = 64;
+__host__ __device__ constexpr int vt_key(int j) {
+  return 16 * (j >> 4) + 8 * ((j & 7) >> 2) + 4 * ((j >> 3) & 1) + (j & 3);
+}
+
 // Launch-side helpers implemented in fva_api.hip.
 int record_hip_error(hipError_t e, const char* what);
 int device_cu_count();

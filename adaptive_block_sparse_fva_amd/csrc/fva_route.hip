@@ -12,23 +12,30 @@
 namespace fva {
 
 // ---------------------------------------------------------------------------
-// 1. Pooling.  One workgroup per (block b, head h, tensor Q|K): the mean of the
-// block's rows, accumulated in fp32.  Memory bound: every byte of Q and K is
-// read exactly once with 16-byte loads, a row's 16-byte chunks spread over
-// consecutive lanes.  The Q workgroups of head 0 also publish the order table,
-// and workgroup (0,0,0) clears the per-head counters for the select kernel.
+// 1. Pooling and re-layout.  One workgroup per (block b, head h, tensor
+// Q|K|V).  Q and K workgroups take the mean of the block's rows, accumulated
+// in fp32; the K workgroups also write the rows in position order (kp), and
+// the V workgroups write V transposed per 64-position sub-block (vt); the
+// layouts are those described with vt_key.  Memory bound: every byte of Q, K
+// and V is read exactly once with 16-byte loads, a row's 16-byte chunks
+// spread over consecutive lanes.  The Q workgroups of head 0 also publish the
+// order table, and workgroup (0,0,0) clears the per-head counters for the
+// select kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void route_pool_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t stride_head, int64_t stride_token, OrderGeo geo, int block,
     int nb, int num_heads, float* __restrict__ qbar, float* __restrict__ kbar,
-    int32_t* __restrict__ order, int32_t* __restrict__ head_count) {
+    int32_t* __restrict__ order, int32_t* __restrict__ head_count,
+    bf16_t* __restrict__ kp, bf16_t* __restrict__ vt) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RG = 256 / CH;   // rows in flight per pass
   constexpr int MAXIT = 128 / RG;
+  constexpr int VP = D + 8;      // padded LDS row of the V transpose
   __shared__ int32_t tok[128];
   __shared__ float part[RG][D];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[VT_KEYS * VP];
 
   const int b = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int tid = threadIdx.x;
@@ -42,26 +49,61 @@ __global__ __launch_bounds__(256) void route_pool_kernel(
     for (int i = tid; i < num_heads; i += 256) head_count[i] = 0;
   __syncthreads();
 
-  const bf16_t* x = (which == 0 ? q : k) + (int64_t)h * stride_head;
+  const int64_t npad = (int64_t)nb * block;
   const int c = tid % CH, rg = tid / CH;
-  u32x4 v[MAXIT];
+  if (which == 2) {
+    // V: per 64-position sub-block, rows into LDS, then columns out
+    const bf16_t* x = v + (int64_t)h * stride_head;
+    for (int sb = 0; sb < block; sb += VT_KEYS) {
+      for (int r = rg; r < VT_KEYS; r += RG) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (sb + r < rb) w = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[sb + r] * stride_token + c * 8);
+        *reinterpret_cast<u32x4*>(&vs[r * VP + c * 8]) = w;
+      }
+      __syncthreads();
+      bf16_t* dst = vt + ((int64_t)h * npad + (int64_t)b * block + sb) * D;
+      for (int i = tid; i < D * (VT_KEYS / 8); i += 256) {
+        const int row = i / (VT_KEYS / 8), jc = i % (VT_KEYS / 8);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)vs[vt_key(jc * 8 + 2 * e) * VP + row] |
+                 ((uint32_t)vs[vt_key(jc * 8 + 2 * e + 1) * VP + row] << 16);
+        *reinterpret_cast<u32x4*>(dst + row * VT_KEYS + jc * 8) = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  const bf16_t* x = (which == 0 ? q : k) + (int64_t)h * stride_head;
+  u32x4 rows[MAXIT];
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
     const int r = rg + it * RG;
     if (r < rb)
-      v[it] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[r] * stride_token + c * 8);
+      rows[it] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[r] * stride_token + c * 8);
     else
-      v[it] = u32x4{0u, 0u, 0u, 0u};
+      rows[it] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (which == 1) {
+    // K rows in position order, zero rows past the end
+    bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int r = rg + it * RG;
+      if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = rows[it];
+    }
   }
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
-    acc[0] += bf16_lo(v[it].x); acc[1] += bf16_hi(v[it].x);
-    acc[2] += bf16_lo(v[it].y); acc[3] += bf16_hi(v[it].y);
-    acc[4] += bf16_lo(v[it].z); acc[5] += bf16_hi(v[it].z);
-    acc[6] += bf16_lo(v[it].w); acc[7] += bf16_hi(v[it].w);
+    acc[0] += bf16_lo(rows[it].x); acc[1] += bf16_hi(rows[it].x);
+    acc[2] += bf16_lo(rows[it].y); acc[3] += bf16_hi(rows[it].y);
+    acc[4] += bf16_lo(rows[it].z); acc[5] += bf16_hi(rows[it].z);
+    acc[6] += bf16_lo(rows[it].w); acc[7] += bf16_hi(rows[it].w);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rg][c * 8 + e] = acc[e];
@@ -258,20 +300,22 @@ __global__ __launch_bounds__(256) void route_select_kernel(
 // ---------------------------------------------------------------------------
 // Launch sequence for fva_route.
 // ---------------------------------------------------------------------------
-int launch_route(const fva_problem& p, int nb, const void* q, const void* k,
+int launch_route(const fva_problem& p, int nb, const void* q, const void* k, const void* v,
                  float* scores, int16_t* ranked, int32_t* row_count,
-                 int32_t* head_count, int32_t* order, float* qbar, float* kbar,
+                 int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
                  float sm_scale, hipStream_t stream) {
   const OrderGeo geo = make_order_geo(p);
-  const dim3 pool_grid(nb, p.num_heads, 2);
+  const dim3 pool_grid(nb, p.num_heads, 3);
+  bf16_t* kp = (bf16_t*)kv;
+  bf16_t* vt = kp + (int64_t)p.num_heads * nb * p.block * p.head_dim;
   if (p.head_dim == 128)
     route_pool_kernel<128><<<pool_grid, 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, p.stride_head, p.stride_token, geo,
-        p.block, nb, p.num_heads, qbar, kbar, order, head_count);
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, p.stride_head, p.stride_token, geo,
+        p.block, nb, p.num_heads, qbar, kbar, order, head_count, kp, vt);
   else
     route_pool_kernel<64><<<pool_grid, 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, p.stride_head, p.stride_token, geo,
-        p.block, nb, p.num_heads, qbar, kbar, order, head_count);
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, p.stride_head, p.stride_token, geo,
+        p.block, nb, p.num_heads, qbar, kbar, order, head_count, kp, vt);
   int st = record_hip_error(hipGetLastError(), "route_pool launch");
   if (st) return st;
 

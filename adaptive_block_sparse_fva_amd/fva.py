@@ -75,6 +75,7 @@ class Sizes(ctypes.Structure):
         ("col_idx_capacity", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("tile_counter_elems", ctypes.c_int32),
+        ("kv_elems", ctypes.c_int64),
     ]
 
 
@@ -94,9 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.fva_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
-    lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
     lib.fva_last_error.argtypes = []
@@ -159,9 +160,11 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def route(prob, q, k, scores, ranked, row_count, head_count, order, workspace, stream=None):
-    st = load_library().fva_route(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(scores), _ptr(ranked),
-                                  _ptr(row_count), _ptr(head_count), _ptr(order), _ptr(workspace),
+def route(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, workspace,
+          stream=None):
+    st = load_library().fva_route(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(scores),
+                                  _ptr(ranked), _ptr(row_count), _ptr(head_count), _ptr(order),
+                                  _ptr(kv), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "fva_route")
 
@@ -174,12 +177,12 @@ def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, tile_order
     _check(st, "fva_plan")
 
 
-def sparse_attn_fwd(prob, q, k, v, order, row_ptr, col_idx, tile_order, tile_counter, o,
+def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, tile_order, tile_counter, o,
                     lse=None, stream=None):
-    st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
-                                            _ptr(order), _ptr(row_ptr), _ptr(col_idx),
-                                            _ptr(tile_order), _ptr(tile_counter), _ptr(o),
-                                            _ptr(lse), _stream(stream))
+    st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(kv), _ptr(order),
+                                            _ptr(row_ptr), _ptr(col_idx), _ptr(tile_order),
+                                            _ptr(tile_counter), _ptr(o), _ptr(lse),
+                                            _stream(stream))
     _check(st, "fva_sparse_attn_fwd")
 
 
@@ -195,6 +198,7 @@ class Buffers:
     head_count: torch.Tensor
     order: torch.Tensor
     workspace: torch.Tensor
+    kv: torch.Tensor
     row_ptr: torch.Tensor
     col_idx: torch.Tensor
     head_count_final: torch.Tensor
@@ -218,6 +222,7 @@ class Buffers:
             order=torch.empty(sz.order_elems, **i32),
             workspace=torch.empty(max(16, sz.workspace_bytes) // 4, dtype=torch.float32,
                                   device=device),
+            kv=torch.empty(sz.kv_elems, dtype=torch.bfloat16, device=device),
             row_ptr=torch.empty(sz.num_rows + 1, **i32),
             col_idx=torch.empty(sz.col_idx_capacity, **i32),
             head_count_final=torch.empty(H, **i32),
@@ -227,24 +232,25 @@ class Buffers:
             lse=torch.empty((H, N), dtype=torch.float32, device=device),
         )
 
-    def route(self, q, k, stream=None):
-        route(self.prob, q, k, self.scores, self.ranked, self.row_count, self.head_count,
-              self.order, self.workspace, stream)
+    def route(self, q, k, v, stream=None):
+        route(self.prob, q, k, v, self.scores, self.ranked, self.row_count, self.head_count,
+              self.order, self.kv, self.workspace, stream)
 
     def plan(self, stream=None):
         plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
              self.head_count_final, self.tile_order, self.tile_counter, stream)
 
-    def attn(self, q, k, v, tile_order=None, with_lse=True, stream=None):
-        sparse_attn_fwd(self.prob, q, k, v, self.order, self.row_ptr, self.col_idx,
+    def attn(self, q, tile_order=None, with_lse=True, stream=None):
+        """Attention over the K/V that the last route() call re-laid out."""
+        sparse_attn_fwd(self.prob, q, self.kv, self.order, self.row_ptr, self.col_idx,
                         self.tile_order if tile_order is None else tile_order, self.tile_counter,
                         self.o, self.lse if with_lse else None, stream)
 
     def run(self, q, k, v, stream=None):
         """One full call of the hot path: route -> plan -> attention."""
-        self.route(q, k, stream)
+        self.route(q, k, v, stream)
         self.plan(stream)
-        self.attn(q, k, v, stream=stream)
+        self.attn(q, stream=stream)
         return self.o
 
 

@@ -173,11 +173,11 @@ def main():
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
-        buf.route(q, k)
+        buf.route(q, k, v)
         e[1].record(stream)
         buf.plan()
         e[2].record(stream)
-        buf.attn(q, k, v)
+        buf.attn(q)
         e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -196,7 +196,10 @@ def main():
     dense_flops = 4.0 * N * N * d * H
     attn_avg_ms = float(t_attn.mean())
     achieved_tflops = kept / (attn_avg_ms * 1e-3) / 1e12
-    route_bytes = 2 * H * N * d * 2 + H * nb * nb * (4 + 2) + H * nb * 4 * 2 + nb * B * 4
+    # route reads Q, K, V once, writes K and V re-laid out, the scores, the
+    # ranking, the counts and the order table
+    route_bytes = (3 * H * N * d * 2 + 2 * H * nb * B * d * 2 + H * nb * nb * (4 + 2)
+                   + H * nb * 4 * 2 + nb * B * 4)
     route_gbs = route_bytes / (float(t_route.mean()) * 1e-3) / 1e9
 
     # one-GPU analog of the load-imbalance factor: tiles list-scheduled onto the

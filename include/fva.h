@@ -5,7 +5,8 @@
  * One call of the hot path is three stream-ordered entry points:
  *
  *   fva_route            video-aware order, pooled Q/K block scores, ranking,
- *                        Top-p cutoff with a Top-k floor, per-head counts
+ *                        Top-p cutoff with a Top-k floor, per-head counts,
+ *                        K and V re-laid out in the order
  *   fva_plan             refill of next-ranked blocks, CSR block mask,
  *                        heaviest-first (LPT) tile order, queue reset
  *   fva_sparse_attn_fwd  block-sparse attention forward over the kept blocks,
@@ -95,6 +96,7 @@ typedef struct fva_sizes_t {
   int64_t col_idx_capacity;  /* H*nb*nb int32 (col_idx, worst case) */
   int64_t workspace_bytes;   /* fva_route workspace */
   int32_t tile_counter_elems;/* 2 uint32 */
+  int64_t kv_elems;          /* 2*H*nb*B*d bf16 (kv) */
 } fva_sizes_t;
 
 /* Host only: validate a problem and report buffer sizes.  Makes no HIP call. */
@@ -107,7 +109,7 @@ int fva_attn_workgroups(const fva_problem* prob, int32_t* out);
 
 /*
  * Routing frontend (FVAttn S3.1; GSRS S5.3, A.4, A.6).
- *   q, k        device bf16 [H][N][d] (strided as above), read only.
+ *   q, k, v     device bf16 [H][N][d] (strided as above), read only.
  *   scores      device float [H][nb][nb], written: s_{h,i,j} =
  *               sm_scale * <mean of Q_h over query block i, mean of K_h over
  *               key block j>, blocks taken in the video-aware order.
@@ -123,13 +125,22 @@ int fva_attn_workgroups(const fva_problem* prob, int32_t* out);
  *               position of the video-aware order, -1 past N (frame-major,
  *               tile_h x tile_w tiles in raster order, raster inside a tile,
  *               edge tiles cut at the border).
+ *   kv          device bf16 [2][H][nb*B][d] (fva_sizes().kv_elems), 16-byte
+ *               aligned, written: K and V of every head permuted into the
+ *               order (GSRS A.6: the permutation that makes blocks
+ *               contiguous), the layout fva_sparse_attn_fwd reads.  Part 0:
+ *               row p of head h = K row of token order[p]; part 1: V
+ *               transposed per 64-position sub-block s, [h][s][c][j] = V of
+ *               token order[64 s + key(j)] at feature c, with
+ *               key(j) = 16(j/16) + 8((j%8)/4) + 4((j/8)%2) + j%4.  Rows of
+ *               positions past N are zero.
  *   workspace   device scratch of workspace_bytes >= fva_sizes().workspace_bytes
  *               (pooled block means); contents are not needed after the call.
  */
 int fva_route(const fva_problem* prob, const void* q, const void* k,
-              float* scores, int16_t* ranked, int32_t* row_count,
-              int32_t* head_count, int32_t* order,
-              void* workspace, size_t workspace_bytes, void* stream);
+              const void* v, float* scores, int16_t* ranked,
+              int32_t* row_count, int32_t* head_count, int32_t* order,
+              void* kv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Plan (FVAttn S3.2-S3.3 on one GPU: the placement step becomes a
@@ -155,7 +166,8 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
  * Block-sparse attention forward (GSRS S3.2, A.1): for every query token of
  * query block i of head h, softmax(sm_scale * q.k) over the tokens of the kept
  * key blocks col_idx[row_ptr[h*nb+i] .. row_ptr[h*nb+i+1]) only, times V.
- *   q, k, v      device bf16, read only.
+ *   q            device bf16 [H][N][d] (strided as above), read only.
+ *   kv           K and V as written by fva_route, read only.
  *   order        device int32 [nb*B] as written by fva_route.
  *   row_ptr, col_idx   CSR mask (each row non-empty, ids in [0, nb)).
  *   tile_order   device int32 [H*nb], a permutation of the tile ids; the
@@ -167,11 +179,11 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
  *   lse          device float [H][N] or NULL, written: natural-log
  *                log-sum-exp of each query's kept logits.
  */
-int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* k,
-                        const void* v, const int32_t* order,
-                        const int32_t* row_ptr, const int32_t* col_idx,
-                        const int32_t* tile_order, uint32_t* tile_counter,
-                        void* o, float* lse, void* stream);
+int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
+                        const int32_t* order, const int32_t* row_ptr,
+                        const int32_t* col_idx, const int32_t* tile_order,
+                        uint32_t* tile_counter, void* o, float* lse,
+                        void* stream);
 
 /* Static text for a status code. */
 const char* fva_status_string(int status);

@@ -42,12 +42,12 @@ def device_inputs(inp):
 def run_chain(prob, q, k, v, tile_order=None, with_lse=True):
     """route -> plan -> attention on the current stream; returns (Buffers, host dict)."""
     buf = F.Buffers.allocate(prob)
-    buf.route(q, k)
+    buf.route(q, k, v)
     buf.plan()
     if tile_order is not None:
-        buf.attn(q, k, v, tile_order=tile_order, with_lse=with_lse)
+        buf.attn(q, tile_order=tile_order, with_lse=with_lse)
     else:
-        buf.attn(q, k, v, with_lse=with_lse)
+        buf.attn(q, with_lse=with_lse)
     torch.cuda.synchronize()
     return buf, host(buf)
 

@@ -108,11 +108,11 @@ def test_entry_points_reject_null_pointers_without_a_device():
     lib = F.load_library()
     p = _ok_problem()
     null = None
-    st = lib.fva_route(ctypes.byref(p), null, null, null, null, null, null, null, null, 0, null)
+    st = lib.fva_route(ctypes.byref(p), *([null] * 10), 0, null)
     assert st == fva.FVA_ERR_ARG
     st = lib.fva_plan(ctypes.byref(p), null, null, null, null, null, null, null, null)
     assert st == fva.FVA_ERR_ARG
-    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 11))
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 10))
     assert st == fva.FVA_ERR_ARG
     assert lib.fva_sizes(None, None) == fva.FVA_ERR_ARG
     assert lib.fva_status_string(fva.FVA_ERR_WORKSPACE) == b"workspace too small"
@@ -122,10 +122,28 @@ def test_route_rejects_small_workspace_before_launch():
     lib = F.load_library()
     p = _ok_problem()
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the check fails first
-    st = lib.fva_route(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, 16, None)
+    st = lib.fva_route(ctypes.byref(p), *([fake] * 10), 16, None)
     assert st == fva.FVA_ERR_WORKSPACE
     mis = ctypes.c_void_p((1 << 20) + 2)
-    st = lib.fva_route(ctypes.byref(p), mis, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    st = lib.fva_route(ctypes.byref(p), mis, *([fake] * 9), 1 << 30, None)
+    assert st == fva.FVA_ERR_ARG
+    # the re-laid-out K/V buffer must be 16-byte aligned too
+    st = lib.fva_route(ctypes.byref(p), *([fake] * 8), ctypes.c_void_p((1 << 20) + 8), fake,
+                       1 << 30, None)
+    assert st == fva.FVA_ERR_ARG
+
+
+def test_kv_size_and_attention_alignment_checks():
+    lib = F.load_library()
+    p = _ok_problem()
+    sz = F.sizes(p)
+    assert sz.kv_elems == 2 * p.num_heads * sz.num_blocks * p.block * p.head_dim
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the checks fail first
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    # q kv order row_ptr col_idx tile_order tile_counter o lse stream
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, mis, *([fake] * 6), None, None)
+    assert st == fva.FVA_ERR_ARG
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, None, *([fake] * 6), None, None)
     assert st == fva.FVA_ERR_ARG
 
 
@@ -134,4 +152,4 @@ def test_binding_refuses_cpu_tensors():
     p = _ok_problem(num_heads=1, seq_len=1024, head_dim=64, grid=(4, 16, 16), block=64, tile=(8, 8))
     t = torch.zeros(16)
     with pytest.raises(F.FvaError):
-        fva.route(p, t, t, t, t, t, t, t, t)
+        fva.route(p, t, t, t, t, t, t, t, t, t, t)

@@ -137,7 +137,7 @@ def test_tile_order_changes_placement_only(name):
     natural = torch.arange(buf.tile_order.numel(), dtype=torch.int32, device="cuda")
     reverse = torch.flip(natural, [0])
     for alt in (natural, reverse):
-        buf.attn(q, k, v, tile_order=alt)
+        buf.attn(q, tile_order=alt)
         torch.cuda.synchronize()
         assert torch.equal(buf.o.view(torch.int16).cpu(), torch.from_numpy(
             res["o"].astype(np.float32)).to(torch.bfloat16).view(torch.int16))
@@ -199,3 +199,31 @@ def test_token_major_layout_matches_head_major():
     got = buf.o.permute(1, 0, 2).float().cpu().numpy()
     np.testing.assert_array_equal(got, ref["o"])
     np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
+
+
+def _vt_key(j):
+    # column j of a V^T sub-tile holds this key position (the layout fva.h documents)
+    return 16 * (j // 16) + 8 * ((j % 8) // 4) + 4 * ((j // 8) % 2) + j % 4
+
+
+@pytest.mark.parametrize("name", ["two_head", "rank480p"])
+def test_kv_relayout_is_the_documented_permutation(name):
+    """fva_route's kv output: K rows and transposed V sub-tiles in position order, bit-exact."""
+    wl = WORKLOADS[name]
+    say(f"[gpu] kv re-layout {name}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    buf, res = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
+    H, N, d, B, nb = wl.num_heads, wl.seq_len, wl.head_dim, wl.block, res["nb"]
+    npad = nb * B
+    order = O.padded_order(O.token_order(wl.grid, wl.tile_hw), B)
+    kv = buf.kv.view(torch.int16).cpu().numpy().view(np.uint16).reshape(2, H, npad, d)
+    valid = order >= 0
+    kp_ref = np.zeros((H, npad, d), np.uint16)
+    kp_ref[:, valid] = inp.k[:, order[valid]]
+    np.testing.assert_array_equal(kv[0], kp_ref)
+    vp = np.zeros((H, npad, d), np.uint16)
+    vp[:, valid] = inp.v[:, order[valid]]
+    cols = np.array([_vt_key(j) for j in range(64)])
+    vt_ref = vp.reshape(H, npad // 64, 64, d)[:, :, cols, :].transpose(0, 1, 3, 2)
+    np.testing.assert_array_equal(kv[1].reshape(H, npad // 64, d, 64), vt_ref)
