@@ -45,7 +45,13 @@ Readings where the pages are silent (each also listed in the design notes):
   * one-GPU SASA: every row gets e_i = min(nb - k_i, floor(k_i * refill / 1000))
     more blocks, the next ones in the ranking;
   * tile order: tiles sorted by kept count descending, then head, then query
-    block (longest-processing-time first).
+    block (longest-processing-time first);
+  * one-GPU placement with split tiles (our adaptation of S3.2's "move work,
+    never change it" to the compute units of one GPU; no page defines it):
+    with S = min(workgroups, MAX_SPLITS / 2) and a = ceil(sum_t k'_t / S), a
+    tile with k'_t >= 2 and 2 k'_t > a is cut into two work items, its first
+    ceil(k'/2) kept blocks and the rest; the work list is every item sorted by
+    item length descending, then tile, then part.
 """
 
 from __future__ import annotations
@@ -56,6 +62,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 FIXED_POINT_BITS = 40
+MAX_SPLITS = 1024  # split tiles one call can hold partial results for
 
 
 # --------------------------------------------------------------------------
@@ -213,6 +220,35 @@ def plan(scores32: np.ndarray, row_count: np.ndarray, refill_per_mille: int) -> 
         "head_count": kept.reshape(H, nqb).sum(axis=1),
         "tile_order": tile_order,
     }
+
+
+def work_items(kept: np.ndarray, workgroups: int, max_splits: int = MAX_SPLITS):
+    """One-GPU placement of the tiles ([FVA] S3.2 adapted to one GPU).
+
+    Tiles much heavier than the mean load of a workgroup cannot be balanced by
+    ordering alone, so each tile with k' >= 2 and 2 k' > ceil(total / S) is
+    cut into two work items (the first ceil(k'/2) of its kept blocks, then the
+    rest), S = min(workgroups, max_splits // 2).  Returns the work list (entries
+    tile * 2 + part, longest item first, then tile, then part), the split slot
+    of every tile (its rank among the split tiles by tile id, -1 if whole) and
+    the number of split tiles.
+    """
+    kept = np.asarray(kept, dtype=np.int64)
+    S = min(int(workgroups), max_splits // 2)
+    avg = -(-int(kept.sum()) // S)
+    split = (kept >= 2) & (2 * kept > avg)
+    slot = np.full(len(kept), -1, dtype=np.int64)
+    slot[split] = np.arange(int(split.sum()))
+    items = []
+    for t, k in enumerate(kept.tolist()):
+        if split[t]:
+            items.append(((k + 1) // 2, t, 0))
+            items.append((k // 2, t, 1))
+        else:
+            items.append((k, t, 0))
+    items.sort(key=lambda x: (-x[0], x[1], x[2]))
+    order = np.array([2 * t + part for _, t, part in items], dtype=np.int64)
+    return order, slot, int(split.sum())
 
 
 def head_workload(head_count: np.ndarray, nb: int) -> np.ndarray:

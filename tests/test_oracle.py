@@ -297,6 +297,45 @@ def test_plan_lpt_order():
             assert a < b  # equal counts: head, then query block
 
 
+def test_work_items_hand_example():
+    # k' = [5, 1, 3, 8], 2 workgroups: total 17, mean load ceil(17/2) = 9, so
+    # tiles with 2k' > 9 (tiles 0 and 3) are cut: 5 -> 3 + 2, 8 -> 4 + 4.
+    # Items (length, tile, part): (4,3,0) (4,3,1) (3,0,0) (3,2,0) (2,0,1) (1,1,0).
+    order, slot, nsplit = O.work_items(np.array([5, 1, 3, 8]), 2)
+    np.testing.assert_array_equal(order, [6, 7, 0, 4, 1, 2])
+    np.testing.assert_array_equal(slot, [0, -1, -1, 1])
+    assert nsplit == 2
+
+
+def test_work_items_invariants():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        rows = int(rng.integers(1, 300))
+        kept = rng.integers(1, 200, rows)
+        if trial % 3 == 0:
+            kept[: rows // 4] = 200  # a heavy head
+        wg = int(rng.integers(1, 700))
+        order, slot, nsplit = O.work_items(kept, wg)
+        S = min(wg, O.MAX_SPLITS // 2)
+        assert nsplit < 2 * S and nsplit <= O.MAX_SPLITS
+        tiles, parts = order // 2, order % 2
+        # every tile once, split tiles twice (parts 0 and 1)
+        counts = np.bincount(tiles, minlength=rows)
+        np.testing.assert_array_equal(counts, np.where(slot >= 0, 2, 1))
+        assert np.all(parts[slot[tiles] < 0] == 0)
+        # split slots number the split tiles in tile-id order
+        np.testing.assert_array_equal(slot[np.flatnonzero(slot >= 0)], np.arange(nsplit))
+        # item lengths cover every kept block and never increase along the list
+        length = np.where(slot[tiles] < 0, kept[tiles],
+                          np.where(parts == 0, (kept[tiles] + 1) // 2, kept[tiles] // 2))
+        assert length.sum() == kept.sum()
+        assert np.all(np.diff(length) <= 0)
+        # with the heavy tiles cut, no item exceeds the mean load per workgroup
+        # unless a single tile is more than twice that mean
+        mean = -(-kept.sum() // S)
+        assert length.max() <= max(mean, (kept.max() + 1) // 2)
+
+
 def test_eq1_eq2_hand_examples():
     np.testing.assert_allclose(O.head_workload(np.array([32, 8]), 16), [2.0, 0.5])
     assert O.imbalance([3, 1, 1, 3]) == pytest.approx(1.5)
