@@ -13,14 +13,14 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
                  float* scores, int16_t* ranked, int32_t* row_count,
                  int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
                  float sm_scale, hipStream_t stream);
-int launch_plan(const fva_problem& p, int nb, const int16_t* ranked,
+int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked,
                 const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
-                int32_t* head_count_final, int32_t* tile_order,
+                int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
                 uint32_t* tile_counter, hipStream_t stream);
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
-                const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
-                float sm_scale, hipStream_t stream);
+                const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
+                void* o, float* lse, void* workspace, float sm_scale, hipStream_t stream);
 int attn_blocks_per_cu(int d, int block);
 
 static thread_local char g_last_error[256] = "";
@@ -106,6 +106,18 @@ static int64_t kv_elems(const fva_problem* p, int nb) {
   return 2 * (int64_t)p->num_heads * nb * p->block * p->head_dim;
 }
 
+// Split tiles one call can produce (fewer than 2 * FVA_MAX_SPLITS / 2).
+static int64_t max_splits(const fva_problem* p, int nb) {
+  const int64_t rows = (int64_t)p->num_heads * nb;
+  return rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
+}
+
+// Partial results of split tiles: per slot and part, B x d floats of
+// unnormalised output plus B maxima and B denominators.
+static int64_t attn_workspace_need(const fva_problem* p, int nb) {
+  return max_splits(p, nb) * 2 * ((int64_t)p->block * p->head_dim + 2 * p->block) * 4;
+}
+
 static float effective_scale(const fva_problem* p) {
   return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
 }
@@ -116,7 +128,7 @@ using namespace fva;
 
 extern "C" {
 
-int fva_version(void) { return 100; }
+int fva_version(void) { return 200; }
 
 const char* fva_status_string(int status) {
   switch (status) {
@@ -146,6 +158,9 @@ int fva_sizes(const fva_problem* prob, fva_sizes_t* out) {
   out->workspace_bytes = workspace_need(prob, nb);
   out->tile_counter_elems = 2;
   out->kv_elems = kv_elems(prob, nb);
+  out->work_order_elems = rows + max_splits(prob, nb);
+  out->plan_meta_elems = 2 + rows + FVA_MAX_SPLITS;
+  out->attn_workspace_bytes = attn_workspace_need(prob, nb);
   return FVA_OK;
 }
 
@@ -181,32 +196,41 @@ int fva_route(const fva_problem* prob, const void* q, const void* k, const void*
 
 int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_count,
              int32_t* row_ptr, int32_t* col_idx, int32_t* head_count_final,
-             int32_t* tile_order, uint32_t* tile_counter, void* stream) {
+             int32_t* work_order, int32_t* plan_meta, uint32_t* tile_counter, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
-  if (!ranked || !row_count || !row_ptr || !col_idx || !head_count_final || !tile_order ||
-      !tile_counter)
+  if (!ranked || !row_count || !row_ptr || !col_idx || !head_count_final || !work_order ||
+      !plan_meta || !tile_counter)
     return FVA_ERR_ARG;
-  return launch_plan(*prob, nb, ranked, row_count, row_ptr, col_idx, head_count_final,
-                     tile_order, tile_counter, (hipStream_t)stream);
+  int grid = 0;
+  st = attn_grid(*prob, nb, &grid);
+  if (st) return st;
+  const int split_s = grid < FVA_MAX_SPLITS / 2 ? grid : FVA_MAX_SPLITS / 2;
+  return launch_plan(*prob, nb, split_s, ranked, row_count, row_ptr, col_idx, head_count_final,
+                     work_order, plan_meta, tile_counter, (hipStream_t)stream);
 }
 
 int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
-                        const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
-                        void* stream) {
+                        const int32_t* work_order, const int32_t* plan_meta,
+                        uint32_t* tile_counter, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
-  if (!q || !kv || !order || !row_ptr || !col_idx || !tile_order || !tile_counter || !o)
+  if (!q || !kv || !order || !row_ptr || !col_idx || !work_order || !plan_meta ||
+      !tile_counter || !o || !workspace)
     return FVA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned16(order)) return FVA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned16(order) ||
+      !aligned16(workspace))
+    return FVA_ERR_ARG;
+  if ((int64_t)workspace_bytes < attn_workspace_need(prob, nb)) return FVA_ERR_WORKSPACE;
   int grid = 0;
   st = attn_grid(*prob, nb, &grid);
   if (st) return st;
-  return launch_attn(*prob, nb, grid, q, kv, order, row_ptr, col_idx, tile_order, tile_counter,
-                     o, lse, effective_scale(prob), (hipStream_t)stream);
+  return launch_attn(*prob, nb, grid, q, kv, order, row_ptr, col_idx, work_order, plan_meta,
+                     tile_counter, o, lse, workspace, effective_scale(prob), (hipStream_t)stream);
 }
 
 }  // extern "C"

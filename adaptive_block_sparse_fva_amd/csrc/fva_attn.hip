@@ -49,8 +49,10 @@ struct AttnArgs {
   const int32_t* order;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  const int32_t* tile_order;
+  const int32_t* work_order;  // tile * 2 + part
+  const int32_t* plan_meta;   // [0] items, [1] split tiles, [2 + t] split slot of tile t
   uint32_t* tile_counter;
+  float* partial;             // per split slot and part: O^T (unnormalised), max, denominator
   int64_t stride_head, stride_token;
   int n, nb, num_tiles;
   int npad;          // nb * B
@@ -114,6 +116,14 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   static_assert(NW * 32 == BLK && SUB * KB == BLK && NI >= 1 && NI * RW == RPW, "tiling");
   static_assert(KB == 64 && NIV >= 1 && NIV * VRW == VRPW, "V^T tiling (64-key sub-blocks)");
   static_assert(NBUF >= 2 && NBUF <= 4, "ring slots");
+#ifndef FVA_S_AHEAD
+#define FVA_S_AHEAD 2
+#endif
+#ifndef FVA_V_AHEAD
+#define FVA_V_AHEAD 0
+#endif
+  constexpr int S_AHEAD = FVA_S_AHEAD;  // k-steps the K operand reads run ahead
+  constexpr int V_AHEAD = FVA_V_AHEAD;  // k-steps the V^T operand reads run ahead (0: compiler's choice)
 
   // K sub-tiles: KB rows (keys) of D elements; V^T sub-tiles: D rows of KB
   // keys; 16-byte chunk c of row r stored at position c ^ swz(r).  The ring slots are separate LDS
@@ -165,15 +175,20 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
     vdma[m] = (uint32_t)(row * KB + ((lane % VCH) ^ swz<VCH>(row)) * 8) * 2u;
   }
   const uint32_t head_bytes = (uint32_t)a.npad * D * 2u;
+  const int num_items = a.plan_meta[0];
 
   for (;;) {
     if (tid == 0) s_tile = (int)atomicAdd(&a.tile_counter[0], 1u);
     __syncthreads();
     const int idx = s_tile;
     __syncthreads();
-    if (idx >= a.num_tiles) break;
+    if (idx >= num_items) break;
 
-    const int t = a.tile_order[idx];
+    // work item: a whole tile, or one part of a split tile's kept list
+    const int item = a.work_order[idx];
+    const int t = item >> 1;
+    const int part = item & 1;
+    const int slot = a.plan_meta[2 + t];
     const int h = t / a.nb;
     const int i = t - h * a.nb;
     const int64_t hoff = (int64_t)h * a.stride_head;
@@ -214,8 +229,17 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) voff[ps] = l32 * KB + ((2 * ps + hf) ^ swz<VCH>(l32)) * 8;
 
-    const int c0 = a.row_ptr[t];
-    const int ncols = a.row_ptr[t + 1] - c0;
+    int c0 = a.row_ptr[t];
+    int ncols = a.row_ptr[t + 1] - c0;
+    if (slot >= 0) {
+      const int first = (ncols + 1) >> 1;
+      if (part) {
+        c0 += first;
+        ncols -= first;
+      } else {
+        ncols = first;
+      }
+    }
     const int nsub = ncols * SUB;
     for (int c = tid; c < ncols; c += BLK * 2) s_cols[c] = a.col_idx[c0 + c];
     __syncthreads();
@@ -280,11 +304,11 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
           s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qf[d], s[kk],
                                                           0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, S_AHEAD * KS, 0);
 #pragma unroll
       for (int d = 0; d < DS; ++d) {
         __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
-        if (d + 2 < DS) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+        if (d + S_AHEAD < DS) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
       }
       __builtin_amdgcn_s_setprio(0);
       // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
@@ -350,6 +374,15 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
           acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[d]), pf, acc_o[d],
                                                              0, 0, 0);
       }
+      if constexpr (V_AHEAD > 0) {
+        // V^T reads run V_AHEAD k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, V_AHEAD * DO, 0);
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps) {
+          __builtin_amdgcn_sched_group_barrier(0x008, DO, 0);
+          if (ps + V_AHEAD < PS) __builtin_amdgcn_sched_group_barrier(0x100, DO, 0);
+        }
+      }
       __builtin_amdgcn_s_setprio(0);
 
       // Sub-block u+1 has landed for every wave and every wave is done with
@@ -370,9 +403,23 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    // ---- normalise and store O (and LSE) for this lane's query ----
+    // ---- normalise and store O (and LSE) for this lane's query, or leave
+    // the part's partial result for the merge ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (qtok >= 0) {
+    if (slot >= 0) {
+      float* pp = a.partial + ((int64_t)slot * 2 + part) * (BLK * D + 2 * BLK);
+      const int qrow = wave * 32 + l32;
+#pragma unroll
+      for (int d = 0; d < DO; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(pp + qrow * D + d * 32 + 8 * g + 4 * hf) =
+              f32x4{acc_o[d][4 * g], acc_o[d][4 * g + 1], acc_o[d][4 * g + 2], acc_o[d][4 * g + 3]};
+      if (hf == 0) {
+        pp[BLK * D + qrow] = m_run;
+        pp[BLK * D + BLK + qrow] = l_tot;
+      }
+    } else if (qtok >= 0) {
       const float inv = 1.0f / l_tot;
       bf16_t* orow = a.o + hoff + (int64_t)qtok * a.stride_token;
 #pragma unroll
@@ -408,6 +455,43 @@ static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
+// Merge of split tiles (one workgroup per split slot): the two parts'
+// partial results combine as in the online softmax (GSRS A.1): with
+// m = max(m0, m1) and weights a_p = 2^(m_p - m), O = (a0 O0 + a1 O1) /
+// (a0 l0 + a1 l1) and LSE = (m + log2(a0 l0 + a1 l1)) ln 2.  Part 0 and part 1
+// enter the formula in that order whichever finished last, so the result does
+// not depend on the order the queue handed them out.
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
+                                                        const int32_t* __restrict__ plan_meta,
+                                                        const int32_t* __restrict__ order, int rows, int nb,
+                                                        int n, int64_t stride_head, int64_t stride_token,
+                                                        bf16_t* __restrict__ o, float* __restrict__ lse) {
+  const int s = blockIdx.x;
+  if (s >= plan_meta[1]) return;
+  const int t = plan_meta[2 + rows + s];
+  const int h = t / nb, i = t - h * nb;
+  constexpr int PART = BLK * D + 2 * BLK;
+  const float* p0 = partial + (int64_t)s * 2 * PART;
+  const float* p1 = p0 + PART;
+  for (int x = threadIdx.x; x < BLK * (D / 4); x += 256) {
+    const int q = x / (D / 4), c = (x % (D / 4)) * 4;
+    const int tok = order[i * BLK + q];
+    if (tok < 0) continue;
+    const float m0 = p0[BLK * D + q], m1 = p1[BLK * D + q];
+    const float m = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l = a0 * p0[BLK * D + BLK + q] + a1 * p1[BLK * D + BLK + q];
+    const float inv = 1.0f / l;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p0 + q * D + c);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(p1 + q * D + c);
+    const u32x2 w = {pack_bf16x2((a0 * x0[0] + a1 * x1[0]) * inv, (a0 * x0[1] + a1 * x1[1]) * inv),
+                     pack_bf16x2((a0 * x0[2] + a1 * x1[2]) * inv, (a0 * x0[3] + a1 * x1[3]) * inv)};
+    *reinterpret_cast<u32x2*>(o + (int64_t)h * stride_head + (int64_t)tok * stride_token + c) = w;
+    if (c == 0 && lse != nullptr) lse[(int64_t)h * n + tok] = (m + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
 template <int D, int BLK>
 static int occupancy_t(int* blocks) {
   return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS>,
@@ -426,10 +510,18 @@ int attn_blocks_per_cu(int d, int block) {
   return b < 1 ? 1 : b;
 }
 
+template <int D, int BLK>
+static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
+  const int grid = rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
+  attn_merge_kernel<D, BLK><<<grid, 256, 0, stream>>>(a.partial, a.plan_meta, a.order, rows, a.nb, a.n,
+                                                      a.stride_head, a.stride_token, a.o, a.lse);
+  return record_hip_error(hipGetLastError(), "attn_merge launch");
+}
+
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
-                const int32_t* tile_order, uint32_t* tile_counter, void* o, float* lse,
-                float sm_scale, hipStream_t stream) {
+                const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
+                void* o, float* lse, void* workspace, float sm_scale, hipStream_t stream) {
   const int npad = nb * p.block;
   const bf16_t* kp = (const bf16_t*)kv;
   const bf16_t* vt = kp + (int64_t)p.num_heads * npad * p.head_dim;
@@ -443,18 +535,32 @@ int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const voi
   a.order = order;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
-  a.tile_order = tile_order;
+  a.work_order = work_order;
+  a.plan_meta = plan_meta;
   a.tile_counter = tile_counter;
+  a.partial = (float*)workspace;
   a.stride_head = p.stride_head;
   a.stride_token = p.stride_token;
   a.n = p.seq_len;
   a.nb = nb;
   a.num_tiles = p.num_heads * nb;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  if (p.head_dim == 128 && p.block == 128) return launch_attn_t<128, 128>(a, grid, stream);
-  if (p.head_dim == 128) return launch_attn_t<128, 64>(a, grid, stream);
-  if (p.block == 128) return launch_attn_t<64, 128>(a, grid, stream);
-  return launch_attn_t<64, 64>(a, grid, stream);
+  const int rows = p.num_heads * nb;
+  int st;
+  if (p.head_dim == 128 && p.block == 128) {
+    if ((st = launch_attn_t<128, 128>(a, grid, stream))) return st;
+    return launch_merge_t<128, 128>(a, rows, stream);
+  }
+  if (p.head_dim == 128) {
+    if ((st = launch_attn_t<128, 64>(a, grid, stream))) return st;
+    return launch_merge_t<128, 64>(a, rows, stream);
+  }
+  if (p.block == 128) {
+    if ((st = launch_attn_t<64, 128>(a, grid, stream))) return st;
+    return launch_merge_t<64, 128>(a, rows, stream);
+  }
+  if ((st = launch_attn_t<64, 64>(a, grid, stream))) return st;
+  return launch_merge_t<64, 64>(a, rows, stream);
 }
 
 }  // namespace fva

@@ -1,4 +1,4 @@
-// Plan kernels: one-GPU slack refill, CSR block mask, heaviest-first tile order.
+// Plan kernels: one-GPU slack refill, CSR block mask, heaviest-first work list.
 //
 // FVAttn paper S3.2: once the mask is materialised the per-head work is known
 // and the placement of work is repaired without changing which blocks are
@@ -17,44 +17,67 @@ __device__ __forceinline__ int refill_count(int k, int nb, int refill_per_mille)
   return k + min(nb - k, (k * refill_per_mille) / 1000);
 }
 
-// One workgroup: final counts, CSR row offsets, per-head totals, LPT order,
-// queue reset.  Rows (tiles) are at most FVA_MAX_TILES = 16384.
+// Sort key of a work item: length descending, then tile, then part.
+__device__ __forceinline__ uint32_t item_key(int len, int tile, int part) {
+  return ((uint32_t)(FVA_MAX_BLOCKS - len) << 15) | ((uint32_t)tile << 1) | (uint32_t)part;
+}
+
+// One workgroup: final counts, CSR row offsets, per-head totals, the split
+// decision, the heaviest-first work list, queue reset.  Rows (tiles) are at
+// most FVA_MAX_TILES = 16384, work items at most rows + FVA_MAX_SPLITS.
+//
+// Placement on one GPU: a tile whose kept count k' exceeds the
+// mean load a = ceil(sum k' / split_s) of a workgroup by more than half
+// (k' >= 2 and 2 k' > a) is cut into two work items (its first ceil(k'/2)
+// kept blocks, then the rest), since no ordering can balance a single item
+// larger than the mean.  Split tiles get slots 0, 1, ... in tile-id order.
+// Fewer than 2 * split_s tiles can qualify, and split_s <= FVA_MAX_SPLITS / 2.
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
-    const int32_t* __restrict__ row_count, int rows, int rpad, int nb,
-    int refill_per_mille, int32_t* __restrict__ row_ptr,
-    int32_t* __restrict__ head_count_final, int32_t* __restrict__ tile_order,
+    const int32_t* __restrict__ row_count, int rows, int nb, int refill_per_mille, int split_s,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_count_final,
+    int32_t* __restrict__ work_order, int32_t* __restrict__ plan_meta,
     uint32_t* __restrict__ tile_counter) {
-  __shared__ uint32_t keys[FVA_MAX_TILES];
+  // at most FVA_MAX_TILES + FVA_MAX_SPLITS - 1 items, padded to a power of two
+  static_assert(FVA_MAX_SPLITS <= FVA_MAX_TILES, "item list fits the padded sort");
+  __shared__ uint32_t keys[2 * FVA_MAX_TILES];
   __shared__ int32_t wave_tot[PLAN_THREADS / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+
+  // exclusive scan across the workgroup; *total gets the sum
+  auto block_scan = [&](int x, int* total) {
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < PLAN_THREADS / 64; ++w) {
+      if (w < wave) base += wave_tot[w];
+      tot += wave_tot[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - x;
+  };
 
   // per-thread contiguous chunk of rows
   const int per = (rows + PLAN_THREADS - 1) / PLAN_THREADS;
   const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
   int local = 0;
   for (int r = r0; r < r1; ++r) local += refill_count(row_count[r], nb, refill_per_mille);
+  int total = 0;
+  int run = block_scan(local, &total);
 
-  // exclusive scan of the chunk sums across the workgroup
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  int run = base + incl - local;
-
-  // row offsets, sort keys ((2048 - k') << 14 | tile) and per-head totals
+  // row offsets and per-head totals
   int head_acc = 0, head_cur = (r0 < r1) ? r0 / nb : -1;
   for (int r = r0; r < r1; ++r) {
     const int kp = refill_count(row_count[r], nb, refill_per_mille);
     row_ptr[r] = run;
     run += kp;
-    keys[r] = ((uint32_t)(FVA_MAX_BLOCKS - kp) << 14) | (uint32_t)r;
     const int hh = r / nb;
     if (hh != head_cur) {
       atomicAdd(&head_count_final[head_cur], head_acc);
@@ -65,14 +88,40 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   }
   if (head_cur >= 0 && head_acc > 0) atomicAdd(&head_count_final[head_cur], head_acc);
   if (r1 == rows && r0 < r1) row_ptr[rows] = run;
-  if (rows == 0 && tid == 0) row_ptr[0] = 0;
-  for (int r = rows + tid; r < rpad; r += PLAN_THREADS) keys[r] = 0xffffffffu;
+
+  // split decision and slots
+  const int mean = (total + split_s - 1) / split_s;
+  auto is_split = [&](int kp) { return kp >= 2 && 2 * kp > mean; };
+  int nsp = 0;
+  for (int r = r0; r < r1; ++r) nsp += is_split(refill_count(row_count[r], nb, refill_per_mille)) ? 1 : 0;
+  int nsplit = 0;
+  int sp = block_scan(nsp, &nsplit);
+
+  // work items: tile r's items start at r + (split tiles before r)
+  for (int r = r0; r < r1; ++r) {
+    const int kp = refill_count(row_count[r], nb, refill_per_mille);
+    const int pos = r + sp;
+    if (is_split(kp)) {
+      plan_meta[2 + r] = sp;
+      plan_meta[2 + rows + sp] = r;
+      keys[pos] = item_key((kp + 1) >> 1, r, 0);
+      keys[pos + 1] = item_key(kp >> 1, r, 1);
+      ++sp;
+    } else {
+      plan_meta[2 + r] = -1;
+      keys[pos] = item_key(kp, r, 0);
+    }
+  }
+  const int nitems = rows + nsplit;
+  int ipad = 2;
+  while (ipad < nitems) ipad <<= 1;
+  for (int x = nitems + tid; x < ipad; x += PLAN_THREADS) keys[x] = 0xffffffffu;
   __syncthreads();
 
-  // bitonic sort, ascending keys = k' descending, then tile id ascending
-  for (int kk = 2; kk <= rpad; kk <<= 1) {
+  // bitonic sort of the item keys, ascending
+  for (int kk = 2; kk <= ipad; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < (rpad >> 1); i += PLAN_THREADS) {
+      for (int i = tid; i < (ipad >> 1); i += PLAN_THREADS) {
         const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
         const int hi = lo | jj;
         const uint32_t a = keys[lo], b = keys[hi];
@@ -85,8 +134,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
       __syncthreads();
     }
   }
-  for (int r = tid; r < rows; r += PLAN_THREADS) tile_order[r] = (int32_t)(keys[r] & 0x3fffu);
+  for (int x = tid; x < nitems; x += PLAN_THREADS) work_order[x] = (int32_t)(keys[x] & 0x7fffu);
   if (tid == 0) {
+    plan_meta[0] = nitems;
+    plan_meta[1] = nsplit;
     atomicExch(&tile_counter[0], 0u);
     atomicExch(&tile_counter[1], 0u);
   }
@@ -142,18 +193,16 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
   }
 }
 
-int launch_plan(const fva_problem& p, int nb, const int16_t* ranked,
+int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked,
                 const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
-                int32_t* head_count_final, int32_t* tile_order,
+                int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
                 uint32_t* tile_counter, hipStream_t stream) {
   const int rows = p.num_heads * nb;
-  int rpad = 2;
-  while (rpad < rows) rpad <<= 1;
   plan_clear_kernel<<<(p.num_heads + 255) / 256, 256, 0, stream>>>(head_count_final, p.num_heads);
   int st = record_hip_error(hipGetLastError(), "plan_clear launch");
   if (st) return st;
-  plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, rows, rpad, nb, p.refill_per_mille,
-                                                   row_ptr, head_count_final, tile_order,
+  plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, rows, nb, p.refill_per_mille, split_s,
+                                                   row_ptr, head_count_final, work_order, plan_meta,
                                                    tile_counter);
   st = record_hip_error(hipGetLastError(), "plan_scan launch");
   if (st) return st;

@@ -26,6 +26,7 @@ FVA_ERR_HIP = 3
 FVA_ERR_WORKSPACE = 4
 FVA_MAX_BLOCKS = 2048
 FVA_MAX_TILES = 16384
+FVA_MAX_SPLITS = 1024
 
 EXPORTED = (
     "fva_sizes",
@@ -76,6 +77,9 @@ class Sizes(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64),
         ("tile_counter_elems", ctypes.c_int32),
         ("kv_elems", ctypes.c_int64),
+        ("work_order_elems", ctypes.c_int64),
+        ("plan_meta_elems", ctypes.c_int64),
+        ("attn_workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -96,8 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
     lib.fva_last_error.argtypes = []
@@ -169,19 +174,21 @@ def route(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, works
     _check(st, "fva_route")
 
 
-def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, tile_order, tile_counter,
-         stream=None):
+def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, work_order, plan_meta,
+         tile_counter, stream=None):
     st = load_library().fva_plan(ctypes.byref(prob), _ptr(ranked), _ptr(row_count), _ptr(row_ptr),
-                                 _ptr(col_idx), _ptr(head_count_final), _ptr(tile_order),
-                                 _ptr(tile_counter), _stream(stream))
+                                 _ptr(col_idx), _ptr(head_count_final), _ptr(work_order),
+                                 _ptr(plan_meta), _ptr(tile_counter), _stream(stream))
     _check(st, "fva_plan")
 
 
-def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, tile_order, tile_counter, o,
-                    lse=None, stream=None):
+def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta, tile_counter, o,
+                    workspace, lse=None, stream=None):
     st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(kv), _ptr(order),
-                                            _ptr(row_ptr), _ptr(col_idx), _ptr(tile_order),
-                                            _ptr(tile_counter), _ptr(o), _ptr(lse),
+                                            _ptr(row_ptr), _ptr(col_idx), _ptr(work_order),
+                                            _ptr(plan_meta), _ptr(tile_counter), _ptr(o),
+                                            _ptr(lse), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
                                             _stream(stream))
     _check(st, "fva_sparse_attn_fwd")
 
@@ -202,8 +209,10 @@ class Buffers:
     row_ptr: torch.Tensor
     col_idx: torch.Tensor
     head_count_final: torch.Tensor
-    tile_order: torch.Tensor
+    work_order: torch.Tensor
+    plan_meta: torch.Tensor
     tile_counter: torch.Tensor
+    attn_workspace: torch.Tensor
     o: torch.Tensor
     lse: torch.Tensor
 
@@ -226,8 +235,11 @@ class Buffers:
             row_ptr=torch.empty(sz.num_rows + 1, **i32),
             col_idx=torch.empty(sz.col_idx_capacity, **i32),
             head_count_final=torch.empty(H, **i32),
-            tile_order=torch.empty(sz.num_rows, **i32),
+            work_order=torch.empty(sz.work_order_elems, **i32),
+            plan_meta=torch.empty(sz.plan_meta_elems, **i32),
             tile_counter=torch.zeros(sz.tile_counter_elems, **i32),
+            attn_workspace=torch.empty(max(16, sz.attn_workspace_bytes) // 4, dtype=torch.float32,
+                                       device=device),
             o=torch.empty((H, N, d), dtype=torch.bfloat16, device=device),
             lse=torch.empty((H, N), dtype=torch.float32, device=device),
         )
@@ -238,13 +250,15 @@ class Buffers:
 
     def plan(self, stream=None):
         plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
-             self.head_count_final, self.tile_order, self.tile_counter, stream)
+             self.head_count_final, self.work_order, self.plan_meta, self.tile_counter, stream)
 
-    def attn(self, q, tile_order=None, with_lse=True, stream=None):
-        """Attention over the K/V that the last route() call re-laid out."""
+    def attn(self, q, work_order=None, with_lse=True, stream=None):
+        """Attention over the K/V that the last route() call re-laid out, the
+        work items taken in the plan's order (or in work_order's)."""
         sparse_attn_fwd(self.prob, q, self.kv, self.order, self.row_ptr, self.col_idx,
-                        self.tile_order if tile_order is None else tile_order, self.tile_counter,
-                        self.o, self.lse if with_lse else None, stream)
+                        self.work_order if work_order is None else work_order, self.plan_meta,
+                        self.tile_counter, self.o, self.attn_workspace,
+                        self.lse if with_lse else None, stream)
 
     def run(self, q, k, v, stream=None):
         """One full call of the hot path: route -> plan -> attention."""

@@ -202,10 +202,18 @@ def main():
                    + H * nb * 4 * 2 + nb * B * 4)
     route_gbs = route_bytes / (float(t_route.mean()) * 1e-3) / 1e9
 
-    # one-GPU analog of the load-imbalance factor: tiles list-scheduled onto the
-    # persistent workgroups, heaviest-first vs natural order
+    # one-GPU analog of the load-imbalance factor: work list-scheduled onto the
+    # persistent workgroups -- the plan's work items (heavy tiles cut in two,
+    # heaviest first), whole tiles heaviest first, whole tiles in natural order
     workers = F.attn_workgroups(prob)
     costs = np.diff(row_ptr)
+    meta = buf.plan_meta.cpu().numpy()
+    items = buf.work_order[: int(meta[0])].cpu().numpy()
+    slot = meta[2: 2 + H * nb]
+    it_tile, it_part = items // 2, items % 2
+    it_cost = np.where(slot[it_tile] < 0, costs[it_tile],
+                       np.where(it_part == 0, (costs[it_tile] + 1) // 2, costs[it_tile] // 2))
+    planned = list_schedule_makespan(it_cost, workers)
     lpt = list_schedule_makespan(np.sort(costs)[::-1], workers)
     natural = list_schedule_makespan(costs, workers)
     ideal = costs.sum() / workers
@@ -269,7 +277,8 @@ def main():
                      "traffic": measured_traffic() if wl.name == "rank480p" else None,
                      "kernel": "sparse_attn_fwd_kernel<128,128,64,2>",
                      "algorithmic_flops_per_launch": kept},
-        "cu_imbalance": {"workgroups": workers, "lpt": round(lpt / ideal, 4),
+        "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
+                         "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4)},
         "dense_reference": dense,
         "cpu_baseline": cpu,

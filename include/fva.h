@@ -63,9 +63,11 @@ enum fva_status {
   FVA_ERR_WORKSPACE = 4     /* workspace smaller than fva_sizes() asks for */
 };
 
-/* Largest supported nb (key blocks per row) and H*nb (rows / tiles). */
+/* Largest supported nb (key blocks per row) and H*nb (rows / tiles), and the
+ * most tiles one call cuts into two work items. */
 #define FVA_MAX_BLOCKS 2048
 #define FVA_MAX_TILES 16384
+#define FVA_MAX_SPLITS 1024
 
 /*
  * The problem statement (FVAttn S2.1: per head h, query block i, key block j;
@@ -97,6 +99,9 @@ typedef struct fva_sizes_t {
   int64_t workspace_bytes;   /* fva_route workspace */
   int32_t tile_counter_elems;/* 2 uint32 */
   int64_t kv_elems;          /* 2*H*nb*B*d bf16 (kv) */
+  int64_t work_order_elems;  /* H*nb + min(H*nb, FVA_MAX_SPLITS) int32 (work_order) */
+  int64_t plan_meta_elems;   /* 2 + H*nb + FVA_MAX_SPLITS int32 (plan_meta) */
+  int64_t attn_workspace_bytes; /* fva_sparse_attn_fwd workspace */
 } fva_sizes_t;
 
 /* Host only: validate a problem and report buffer sizes.  Makes no HIP call. */
@@ -144,7 +149,7 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
 
 /*
  * Plan (FVAttn S3.2-S3.3 on one GPU: the placement step becomes a
- * heaviest-first tile queue, slack augmentation a per-row refill).
+ * heaviest-first work queue, slack augmentation a per-row refill).
  *   ranked, row_count   as written by fva_route, read only.
  *   row_ptr      device int32 [H*nb + 1], written: CSR row offsets of the
  *                final mask; row (h, i) keeps k'_i = k_i + e_i blocks with
@@ -153,14 +158,26 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
  *                suffices), written: the first k'_i ranked key blocks of each
  *                row, ascending.
  *   head_count_final  device int32 [H], written: sum of k'_i per head.
- *   tile_order   device int32 [H*nb], written: tile ids h*nb + i sorted by
- *                k'_i descending, then h, then i.
+ *   work_order   device int32 [work_order_elems], written: the work items,
+ *                entries tile * 2 + part (tile id h*nb + i), longest first,
+ *                then tile, then part.  With W = fva_attn_workgroups(),
+ *                S = min(W, FVA_MAX_SPLITS / 2) and a = ceil(sum k' / S), a
+ *                tile with k' >= 2 and 2 k' > a is two items: part 0 = its
+ *                first ceil(k'/2) kept blocks, part 1 = the rest; any other
+ *                tile is one item (part 0, all its blocks).  Splitting only
+ *                moves work between compute units; what is computed is the
+ *                same.
+ *   plan_meta    device int32 [plan_meta_elems], written: [0] number of work
+ *                items, [1] number of split tiles ns, [2 + t] split slot of
+ *                tile t (its rank among split tiles by tile id) or -1,
+ *                [2 + H*nb + s] tile of split slot s (s < ns).
  *   tile_counter device uint32 [2], written: reset to {0, 0}.
+ * Queries the device for W (FVA_ERR_HIP without one).
  */
 int fva_plan(const fva_problem* prob, const int16_t* ranked,
              const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
-             int32_t* head_count_final, int32_t* tile_order,
-             uint32_t* tile_counter, void* stream);
+             int32_t* head_count_final, int32_t* work_order,
+             int32_t* plan_meta, uint32_t* tile_counter, void* stream);
 
 /*
  * Block-sparse attention forward (GSRS S3.2, A.1): for every query token of
@@ -170,20 +187,29 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
  *   kv           K and V as written by fva_route, read only.
  *   order        device int32 [nb*B] as written by fva_route.
  *   row_ptr, col_idx   CSR mask (each row non-empty, ids in [0, nb)).
- *   tile_order   device int32 [H*nb], a permutation of the tile ids; the
- *                queue hands tiles out in this order.  Any permutation gives
- *                bitwise the same o and lse.
+ *   work_order, plan_meta   as written by fva_plan; the queue hands the
+ *                work items out in work_order's order.  Any permutation of
+ *                the first plan_meta[0] entries gives bitwise the same o and
+ *                lse.  The two parts of a split tile each leave their
+ *                partial result (unnormalised output, running maximum and
+ *                denominator) in the workspace, and a second kernel merges
+ *                them and writes that tile's o and lse.
  *   tile_counter device uint32 [2], must be {0, 0} on entry (fva_plan leaves
  *                it so); the kernel leaves it {0, 0} again on exit.
  *   o            device bf16 [H][N][d] (strided like q), written.
  *   lse          device float [H][N] or NULL, written: natural-log
  *                log-sum-exp of each query's kept logits.
+ *   workspace    device scratch of workspace_bytes >=
+ *                fva_sizes().attn_workspace_bytes, 16-byte aligned: the
+ *                partial results of split tiles; contents are not needed
+ *                after the call.
  */
 int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* order, const int32_t* row_ptr,
-                        const int32_t* col_idx, const int32_t* tile_order,
-                        uint32_t* tile_counter, void* o, float* lse,
-                        void* stream);
+                        const int32_t* col_idx, const int32_t* work_order,
+                        const int32_t* plan_meta, uint32_t* tile_counter,
+                        void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* fva_status_string(int status);

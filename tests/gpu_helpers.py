@@ -39,13 +39,13 @@ def device_inputs(inp):
     return to_device(inp.q), to_device(inp.k), to_device(inp.v)
 
 
-def run_chain(prob, q, k, v, tile_order=None, with_lse=True):
+def run_chain(prob, q, k, v, work_order=None, with_lse=True):
     """route -> plan -> attention on the current stream; returns (Buffers, host dict)."""
     buf = F.Buffers.allocate(prob)
     buf.route(q, k, v)
     buf.plan()
-    if tile_order is not None:
-        buf.attn(q, tile_order=tile_order, with_lse=with_lse)
+    if work_order is not None:
+        buf.attn(q, work_order=work_order, with_lse=with_lse)
     else:
         buf.attn(q, with_lse=with_lse)
     torch.cuda.synchronize()
@@ -56,6 +56,7 @@ def host(buf) -> dict:
     H, nb = buf.prob.num_heads, buf.nb
     rows = H * nb
     row_ptr = buf.row_ptr.cpu().numpy().astype(np.int64)
+    meta = buf.plan_meta.cpu().numpy().astype(np.int64)
     return {
         "nb": nb,
         "order": buf.order.cpu().numpy().astype(np.int64),
@@ -66,7 +67,8 @@ def host(buf) -> dict:
         "row_ptr": row_ptr,
         "col_idx": buf.col_idx[: int(row_ptr[-1])].cpu().numpy().astype(np.int64),
         "head_count_final": buf.head_count_final.cpu().numpy().astype(np.int64),
-        "tile_order": buf.tile_order.cpu().numpy().astype(np.int64),
+        "plan_meta": meta,
+        "work_order": buf.work_order[: int(meta[0])].cpu().numpy().astype(np.int64),
         "tile_counter": buf.tile_counter.cpu().numpy(),
         "o": buf.o.float().cpu().numpy().astype(np.float64),
         "lse": buf.lse.cpu().numpy().astype(np.float64),

@@ -110,9 +110,9 @@ def test_entry_points_reject_null_pointers_without_a_device():
     null = None
     st = lib.fva_route(ctypes.byref(p), *([null] * 10), 0, null)
     assert st == fva.FVA_ERR_ARG
-    st = lib.fva_plan(ctypes.byref(p), null, null, null, null, null, null, null, null)
+    st = lib.fva_plan(ctypes.byref(p), *([null] * 9))
     assert st == fva.FVA_ERR_ARG
-    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 10))
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 11), 0, null)
     assert st == fva.FVA_ERR_ARG
     assert lib.fva_sizes(None, None) == fva.FVA_ERR_ARG
     assert lib.fva_status_string(fva.FVA_ERR_WORKSPACE) == b"workspace too small"
@@ -133,18 +133,37 @@ def test_route_rejects_small_workspace_before_launch():
     assert st == fva.FVA_ERR_ARG
 
 
-def test_kv_size_and_attention_alignment_checks():
-    lib = F.load_library()
+def test_sizes_of_kv_plan_and_attention_buffers():
     p = _ok_problem()
     sz = F.sizes(p)
+    rows = p.num_heads * sz.num_blocks
     assert sz.kv_elems == 2 * p.num_heads * sz.num_blocks * p.block * p.head_dim
+    splits = min(rows, fva.FVA_MAX_SPLITS)
+    assert sz.work_order_elems == rows + splits
+    assert sz.plan_meta_elems == 2 + rows + fva.FVA_MAX_SPLITS
+    assert sz.attn_workspace_bytes == splits * 2 * (p.block * p.head_dim + 2 * p.block) * 4
+    small = F.sizes(_ok_problem(num_heads=1, seq_len=1024, head_dim=64, grid=(4, 16, 16), block=64,
+                                tile=(8, 8)))
+    assert small.work_order_elems == 32 and small.attn_workspace_bytes == 16 * 2 * (64 * 64 + 128) * 4
+
+
+def test_attention_argument_checks_before_launch():
+    lib = F.load_library()
+    p = _ok_problem()
+    need = F.sizes(p).attn_workspace_bytes
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the checks fail first
     mis = ctypes.c_void_p((1 << 20) + 8)
-    # q kv order row_ptr col_idx tile_order tile_counter o lse stream
-    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, mis, *([fake] * 6), None, None)
-    assert st == fva.FVA_ERR_ARG
-    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, None, *([fake] * 6), None, None)
-    assert st == fva.FVA_ERR_ARG
+
+    def call(kv=fake, ws=fake, nbytes=need):
+        # q kv order row_ptr col_idx work_order plan_meta tile_counter o lse workspace bytes stream
+        return lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, kv, *([fake] * 6), fake, None, ws,
+                                       nbytes, None)
+
+    assert call(kv=mis) == fva.FVA_ERR_ARG
+    assert call(kv=None) == fva.FVA_ERR_ARG
+    assert call(ws=mis) == fva.FVA_ERR_ARG
+    assert call(ws=None) == fva.FVA_ERR_ARG
+    assert call(nbytes=need - 1) == fva.FVA_ERR_WORKSPACE
 
 
 def test_binding_refuses_cpu_tensors():

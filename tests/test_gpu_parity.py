@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import adaptive_block_sparse_fva_amd as F
 import oracle as O
 from gpu_helpers import (LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, S_REL, device_inputs, f64_inputs,
                          problem_for, run_chain, sample_tiles, say, tile_rows)
@@ -58,7 +59,15 @@ def check_routing_and_plan(wl, inp, res, p, refill):
     np.testing.assert_array_equal(res["row_ptr"], pl["row_ptr"])
     np.testing.assert_array_equal(res["col_idx"], pl["col_idx"])
     np.testing.assert_array_equal(res["head_count_final"], pl["head_count"])
-    np.testing.assert_array_equal(res["tile_order"], pl["tile_order"])
+    # placement: split tiles and the heaviest-first work list, for the
+    # workgroup count the attention launch uses
+    rows = H * nb
+    work, slot, nsplit = O.work_items(pl["kept"], F.attn_workgroups(problem_for(wl, p, refill)))
+    meta = res["plan_meta"]
+    assert meta[0] == rows + nsplit and meta[1] == nsplit
+    np.testing.assert_array_equal(meta[2: 2 + rows], slot)
+    np.testing.assert_array_equal(meta[2 + rows: 2 + rows + nsplit], np.flatnonzero(slot >= 0))
+    np.testing.assert_array_equal(res["work_order"], work)
     np.testing.assert_array_equal(res["tile_counter"], [0, 0])
     return pl
 
@@ -127,17 +136,19 @@ def test_p_zero_is_pure_top_k():
 
 
 @pytest.mark.parametrize("name", ["two_head", "rank480p"])
-def test_tile_order_changes_placement_only(name):
+def test_work_order_changes_placement_only(name):
     """Any queue order gives bitwise the same output (placement, not computation)."""
     wl = WORKLOADS[name]
     say(f"[gpu] LPT vs natural tile order {name}")
     inp = make_inputs(wl)
     q, k, v = device_inputs(inp)
     buf, res = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
-    natural = torch.arange(buf.tile_order.numel(), dtype=torch.int32, device="cuda")
-    reverse = torch.flip(natural, [0])
-    for alt in (natural, reverse):
-        buf.attn(q, tile_order=alt)
+    items = res["work_order"]
+    assert res["plan_meta"][1] > 0, "the workload should have split tiles"
+    by_tile = torch.from_numpy(np.sort(items).astype(np.int32)).cuda()
+    reverse = torch.flip(by_tile, [0])
+    for alt in (by_tile, reverse):
+        buf.attn(q, work_order=alt)
         torch.cuda.synchronize()
         assert torch.equal(buf.o.view(torch.int16).cpu(), torch.from_numpy(
             res["o"].astype(np.float32)).to(torch.bfloat16).view(torch.int16))
@@ -152,7 +163,7 @@ def test_repeat_calls_are_deterministic():
     q, k, v = device_inputs(inp)
     _, a = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
     _, b = run_chain(problem_for(wl, wl.top_p[0]), q, k, v)
-    for key in ("order", "scores", "ranked", "row_count", "row_ptr", "col_idx", "tile_order",
+    for key in ("order", "scores", "ranked", "row_count", "row_ptr", "col_idx", "work_order",
                 "o", "lse"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
