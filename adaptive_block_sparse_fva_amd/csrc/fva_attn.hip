@@ -177,12 +177,12 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   const uint32_t head_bytes = (uint32_t)a.npad * D * 2u;
   const int num_items = a.plan_meta[0];
 
-  for (;;) {
-    if (tid == 0) s_tile = (int)atomicAdd(&a.tile_counter[0], 1u);
-    __syncthreads();
-    const int idx = s_tile;
-    __syncthreads();
-    if (idx >= num_items) break;
+  // Work items: workgroup w starts with item w (so the workgroups do not all
+  // hit the counter at launch); later items come from the queue counter,
+  // offset by the grid size, claimed when a workgroup becomes free (claiming
+  // earlier would reserve items for busy workgroups and unbalance the tail).
+  int idx = blockIdx.x;
+  while (idx < num_items) {
 
     // work item: a whole tile, or one part of a split tile's kept list
     const int item = a.work_order[idx];
@@ -433,16 +433,10 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       if (hf == 0 && a.lse != nullptr)
         a.lse[(int64_t)h * a.n + qtok] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     }
-  }
-
-  // Queue drain: the last workgroup to leave resets the counters, so the
-  // buffer is {0, 0} again for the next call.
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(&a.tile_counter[1], 1u);
-    if (done == gridDim.x - 1) {
-      atomicExch(&a.tile_counter[0], 0u);
-      atomicExch(&a.tile_counter[1], 0u);
-    }
+    if (tid == 0) s_tile = (int)gridDim.x + (int)atomicAdd(&a.tile_counter[0], 1u);
+    __syncthreads();  // every wave is past its last use of s_cols; s_tile is set
+    idx = s_tile;
+    __syncthreads();
   }
 }
 
@@ -455,7 +449,8 @@ static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
-// Merge of split tiles (one workgroup per split slot): the two parts'
+// Merge of split tiles (one workgroup per split slot), run after the attention
+// launch (which also resets the queue counter here): the two parts'
 // partial results combine as in the online softmax (GSRS A.1): with
 // m = max(m0, m1) and weights a_p = 2^(m_p - m), O = (a0 O0 + a1 O1) /
 // (a0 l0 + a1 l1) and LSE = (m + log2(a0 l0 + a1 l1)) ln 2.  Part 0 and part 1
@@ -466,8 +461,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
                                                         const int32_t* __restrict__ plan_meta,
                                                         const int32_t* __restrict__ order, int rows, int nb,
                                                         int n, int64_t stride_head, int64_t stride_token,
-                                                        bf16_t* __restrict__ o, float* __restrict__ lse) {
+                                                        bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                        uint32_t* __restrict__ tile_counter) {
   const int s = blockIdx.x;
+  // the attention launch has finished: reset the queue for the next call
+  if (s == 0 && threadIdx.x == 0) {
+    atomicExch(&tile_counter[0], 0u);
+    atomicExch(&tile_counter[1], 0u);
+  }
   if (s >= plan_meta[1]) return;
   const int t = plan_meta[2 + rows + s];
   const int h = t / nb, i = t - h * nb;
@@ -514,7 +515,8 @@ template <int D, int BLK>
 static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
   const int grid = rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
   attn_merge_kernel<D, BLK><<<grid, 256, 0, stream>>>(a.partial, a.plan_meta, a.order, rows, a.nb, a.n,
-                                                      a.stride_head, a.stride_token, a.o, a.lse);
+                                                      a.stride_head, a.stride_token, a.o, a.lse,
+                                                      a.tile_counter);
   return record_hip_error(hipGetLastError(), "attn_merge launch");
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/fva.h"
 
 namespace fva {
@@ -117,6 +119,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int VT_KEYS = 64;
 __host__ __device__ constexpr int vt_key(int j) {
   return 16 * (j >> 4) + 8 * ((j & 7) >> 2) + 4 * ((j >> 3) & 1) + (j & 3);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Launch-side helpers implemented in fva_api.hip.

@@ -72,21 +72,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   int total = 0;
   int run = block_scan(local, &total);
 
-  // row offsets and per-head totals
-  int head_acc = 0, head_cur = (r0 < r1) ? r0 / nb : -1;
+  // row offsets, then per-head totals from them (the stores are complete and
+  // visible to the workgroup after the barrier inside the next scan)
   for (int r = r0; r < r1; ++r) {
-    const int kp = refill_count(row_count[r], nb, refill_per_mille);
     row_ptr[r] = run;
-    run += kp;
-    const int hh = r / nb;
-    if (hh != head_cur) {
-      atomicAdd(&head_count_final[head_cur], head_acc);
-      head_cur = hh;
-      head_acc = 0;
-    }
-    head_acc += kp;
+    run += refill_count(row_count[r], nb, refill_per_mille);
   }
-  if (head_cur >= 0 && head_acc > 0) atomicAdd(&head_count_final[head_cur], head_acc);
   if (r1 == rows && r0 < r1) row_ptr[rows] = run;
 
   // split decision and slots
@@ -96,6 +87,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   for (int r = r0; r < r1; ++r) nsp += is_split(refill_count(row_count[r], nb, refill_per_mille)) ? 1 : 0;
   int nsplit = 0;
   int sp = block_scan(nsp, &nsplit);
+  for (int hh = tid; hh < rows / nb; hh += PLAN_THREADS)
+    head_count_final[hh] = row_ptr[(hh + 1) * nb] - row_ptr[hh * nb];
 
   // work items: tile r's items start at r + (split tiles before r)
   for (int r = r0; r < r1; ++r) {
@@ -118,7 +111,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   for (int x = nitems + tid; x < ipad; x += PLAN_THREADS) keys[x] = 0xffffffffu;
   __syncthreads();
 
-  // bitonic sort of the item keys, ascending
+  // bitonic sort of the item keys, ascending.  Pair index i maps to the
+  // elements lo, lo | jj; for jj < 64 the 64 pairs of one wave stay inside
+  // one run of 128 elements, so those passes only order the wave's own LDS
+  // accesses, and the workgroup synchronises once per merge level and after
+  // every wider pass.
   for (int kk = 2; kk <= ipad; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
       for (int i = tid; i < (ipad >> 1); i += PLAN_THREADS) {
@@ -131,8 +128,15 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
           keys[hi] = a;
         }
       }
-      __syncthreads();
+      if (jj >= 64) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
+    __syncthreads();
   }
   for (int x = tid; x < nitems; x += PLAN_THREADS) work_order[x] = (int32_t)(keys[x] & 0x7fffu);
   if (tid == 0) {
@@ -141,12 +145,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
     atomicExch(&tile_counter[0], 0u);
     atomicExch(&tile_counter[1], 0u);
   }
-}
-
-// Clears the per-head totals before plan_scan accumulates into them.
-__global__ void plan_clear_kernel(int32_t* __restrict__ head_count_final, int num_heads) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < num_heads; i += gridDim.x * blockDim.x)
-    head_count_final[i] = 0;
 }
 
 // One workgroup per row: mark the first k'_i ranked key blocks in an LDS
@@ -198,13 +196,10 @@ int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked
                 int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
                 uint32_t* tile_counter, hipStream_t stream) {
   const int rows = p.num_heads * nb;
-  plan_clear_kernel<<<(p.num_heads + 255) / 256, 256, 0, stream>>>(head_count_final, p.num_heads);
-  int st = record_hip_error(hipGetLastError(), "plan_clear launch");
-  if (st) return st;
   plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, rows, nb, p.refill_per_mille, split_s,
                                                    row_ptr, head_count_final, work_order, plan_meta,
                                                    tile_counter);
-  st = record_hip_error(hipGetLastError(), "plan_scan launch");
+  int st = record_hip_error(hipGetLastError(), "plan_scan launch");
   if (st) return st;
   plan_fill_kernel<<<rows, 256, 0, stream>>>(ranked, row_ptr, nb, col_idx);
   return record_hip_error(hipGetLastError(), "plan_fill launch");

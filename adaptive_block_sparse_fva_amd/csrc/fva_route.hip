@@ -32,10 +32,8 @@ __global__ __launch_bounds__(256) void route_pool_kernel(
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RG = 256 / CH;   // rows in flight per pass
   constexpr int MAXIT = 128 / RG;
-  constexpr int VP = D + 8;      // padded LDS row of the V transpose
   __shared__ int32_t tok[128];
   __shared__ float part[RG][D];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[VT_KEYS * VP];
 
   const int b = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int tid = threadIdx.x;
@@ -52,26 +50,37 @@ __global__ __launch_bounds__(256) void route_pool_kernel(
   const int64_t npad = (int64_t)nb * block;
   const int c = tid % CH, rg = tid / CH;
   if (which == 2) {
-    // V: per 64-position sub-block, rows into LDS, then columns out
+    // V, transposed per 64-position sub-block: a thread gathers the 16-byte
+    // chunk dc (features 8dc .. 8dc+7) of the 8 keys that make up output
+    // chunk jc (columns 8jc .. 8jc+7), transposes the 8 x 8 bf16 block in
+    // registers and writes 8 rows of 16 bytes.  The 8 keys of chunk jc are
+    // vt_key(8jc + e) = 16(jc/2) + 4(jc%2) + 8(e/4) + e%4.
+    constexpr int DCH = D / 8;
+    constexpr int PER_SB = (VT_KEYS / 8) * DCH;
     const bf16_t* x = v + (int64_t)h * stride_head;
-    for (int sb = 0; sb < block; sb += VT_KEYS) {
-      for (int r = rg; r < VT_KEYS; r += RG) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (sb + r < rb) w = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[sb + r] * stride_token + c * 8);
-        *reinterpret_cast<u32x4*>(&vs[r * VP + c * 8]) = w;
-      }
-      __syncthreads();
-      bf16_t* dst = vt + ((int64_t)h * npad + (int64_t)b * block + sb) * D;
-      for (int i = tid; i < D * (VT_KEYS / 8); i += 256) {
-        const int row = i / (VT_KEYS / 8), jc = i % (VT_KEYS / 8);
-        uint32_t w[4];
+    for (int w = tid; w < (block / VT_KEYS) * PER_SB; w += 256) {
+      const int sb = w / PER_SB, rem = w % PER_SB;
+      const int jc = rem / DCH, dc = rem % DCH;
+      const int k0 = sb * VT_KEYS + 16 * (jc >> 1) + 4 * (jc & 1);
+      u32x4 in[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = (uint32_t)vs[vt_key(jc * 8 + 2 * e) * VP + row] |
-                 ((uint32_t)vs[vt_key(jc * 8 + 2 * e + 1) * VP + row] << 16);
-        *reinterpret_cast<u32x4*>(dst + row * VT_KEYS + jc * 8) = u32x4{w[0], w[1], w[2], w[3]};
+      for (int e = 0; e < 8; ++e) {
+        const int key = k0 + 8 * (e >> 2) + (e & 3);
+        in[e] = u32x4{0u, 0u, 0u, 0u};
+        if (key < rb) in[e] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[key] * stride_token + dc * 8);
       }
-      __syncthreads();
+      bf16_t* dst = vt + ((int64_t)h * npad + (int64_t)b * block + sb * VT_KEYS) * D + (8 * dc) * VT_KEYS + jc * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // feature 8dc + i of keys e = 0..7: the low (i even) or high (i odd)
+        // half of dword i/2 of each key's chunk, paired two keys per dword
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr)
+          o[pr] = __builtin_amdgcn_perm(in[2 * pr + 1][i >> 1], in[2 * pr][i >> 1], sel);
+        *reinterpret_cast<u32x4*>(dst + i * VT_KEYS) = u32x4{o[0], o[1], o[2], o[3]};
+      }
     }
     return;
   }
@@ -178,81 +187,92 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Workgroup-wide exclusive scan of one uint64 per thread (256 threads).
-__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t x, uint64_t* wave_tot,
-                                                             uint64_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  uint64_t base = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) base += wave_tot[w];
-    all += wave_tot[w];
-  }
-  *total = all;
-  return base + incl - x;
+// Inverse of orderable (with -0.0 already folded onto +0.0).
+__device__ __forceinline__ float from_orderable(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
+  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)x, d, 64);
+  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(x >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---------------------------------------------------------------------------
-// 3. Ranking and cutoff.  One workgroup per (query block i, head h) row:
-//   - keys (orderable(s_j) << 32) | (2^32-1-j) sorted descending with a
-//     bitonic network in LDS: score descending, equal scores by lower id;
+// 3. Ranking and cutoff.  One wave per (query block i, head h) row at a time,
+// SEL_ROWS consecutive rows per wave and four waves per workgroup; the sort
+// and the scan use no LDS and no barriers:
+//   - keys (orderable(s_j) << 32) | (2^32-1-j), element x = 64e + lane held
+//     in register e of the lane, sorted descending by a bitonic network
+//     (strides below 64 between lanes, larger strides between registers):
+//     score descending, equal scores by lower id;
 //   - weights w_r = rint(exp(s_(r) - s_(0)) * 2^40) in fp64, an exact integer
 //     inclusive scan along the ranking, target T = fl(p * W);
 //   - k_p = 1 + #{r : prefix_r < ceil(T)}, k_i = max(k_p, min(k_min, nb)).
-// Integer prefix sums make the cutoff independent of summation order.
+// Integer prefix sums make the cutoff independent of summation order.  The
+// per-head sums of k_i are accumulated per wave and per workgroup before one
+// atomic add per head touched (same-address atomics from many workgroups
+// serialise, about 10 ns each).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_select_kernel(
-    const float* __restrict__ scores, int nb, int npad, float top_p, int k_min,
-    int16_t* __restrict__ ranked, int32_t* __restrict__ row_count,
-    int32_t* __restrict__ head_count) {
-  __shared__ uint64_t keys[FVA_MAX_BLOCKS];
-  __shared__ float srow[FVA_MAX_BLOCKS];
-  __shared__ uint64_t wave_tot[4];
-  __shared__ int32_t wave_cnt[4];
+constexpr int SEL_ROWS = 1;
 
-  const int h = blockIdx.y;
-  const int row = h * nb + blockIdx.x;
-  const int tid = threadIdx.x;
+template <int E>  // keys per lane: the row padded to 64 E >= nb slots
+__device__ __forceinline__ int select_row(const float* __restrict__ scores, int nb, int row, float top_p,
+                                          int k_min, int16_t* __restrict__ ranked, int lane) {
+  constexpr int NP = 64 * E;
+  constexpr int LOG = __builtin_ctz(NP);
   const float* s = scores + (int64_t)row * nb;
 
-  for (int j = tid; j < npad; j += 256) {
-    if (j < nb) {
-      const float f = s[j];
-      srow[j] = f;
-      keys[j] = ((uint64_t)orderable(f) << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
-    } else {
-      keys[j] = 0ull;
-    }
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = e * 64 + lane;
+    key[e] = x < nb ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x)) : 0ull;
   }
-  __syncthreads();
 
-  for (int kk = 2; kk <= npad; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < (npad >> 1); i += 256) {
-        const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
-        const int hi = lo | jj;
-        const uint64_t a = keys[lo], b = keys[hi];
-        const bool desc = (lo & kk) == 0;
-        if ((a < b) == desc) {
-          keys[lo] = b;
-          keys[hi] = a;
+  // bitonic sort, descending over x = 64e + lane
+  static_for<1, LOG + 1>([&](auto kl) {
+    constexpr int KK = 1 << decltype(kl)::value;
+    static_for<0, decltype(kl)::value>([&](auto jl) {
+      constexpr int JJ = KK >> (decltype(jl)::value + 1);
+      if constexpr (JJ >= 64) {
+        constexpr int JE = JJ / 64;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & JE) == 0) {
+            const bool desc = ((e * 64 + lane) & KK) == 0;
+            const uint64_t a = key[e], b = key[e | JE];
+            if ((a < b) == desc) {
+              key[e] = b;
+              key[e | JE] = a;
+            }
+          }
+        }
+      } else {
+        const bool lower = (lane & JJ) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool desc = ((e * 64 + lane) & KK) == 0;
+          const uint64_t a = key[e], b = shfl_xor_u64(a, JJ);
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          key[e] = (lower == desc) ? hi : lo;
         }
       }
-      __syncthreads();
-    }
-  }
+    });
+  });
 
   int16_t* rk = ranked + (int64_t)row * nb;
-  for (int r = tid; r < nb; r += 256)
-    rk[r] = (int16_t)(0xffffffffu - (uint32_t)(keys[r] & 0xffffffffull));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = e * 64 + lane;
+    if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
+  }
 
   int kp;
   const float p = top_p;
@@ -261,45 +281,73 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   } else if (!(p > 0.0f)) {
     kp = 0;
   } else {
-    // weights along the ranking (pad slots weigh 0)
-    const double smax = (double)srow[0xffffffffu - (uint32_t)(keys[0] & 0xffffffffull)];
-    __syncthreads();  // every thread has read keys[0]; keys[] is reused for weights
-    for (int r = tid; r < nb; r += 256) {
-      const double sr = (double)srow[0xffffffffu - (uint32_t)(keys[r] & 0xffffffffull)];
-      keys[r] = (uint64_t)rint(exp(sr - smax) * 1099511627776.0);  // 2^40
+    // weights along the ranking (pad slots weigh 0), exact integer scan
+    const uint32_t top = (uint32_t)(__shfl((int)(uint32_t)(key[0] >> 32), 0, 64));
+    const double smax = (double)from_orderable(top);
+    uint64_t prefix[E];
+    uint64_t carry = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int x = e * 64 + lane;
+      const double sr = (double)from_orderable((uint32_t)(key[e] >> 32));
+      const uint64_t w = x < nb ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
+      uint64_t incl = w;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t y = shfl_up_u64(incl, off);
+        if (lane >= off) incl += y;
+      }
+      prefix[e] = carry + incl;
+      const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)incl, 63, 64);
+      const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(incl >> 32), 63, 64);
+      carry += ((uint64_t)thi << 32) | tlo;
     }
-    __syncthreads();
-    // contiguous segment of the ranking per thread, exact integer scan
-    const int ept = (nb + 255) / 256;
-    const int r0 = min(nb, tid * ept), r1 = min(nb, r0 + ept);
-    uint64_t local = 0;
-    for (int r = r0; r < r1; ++r) local += keys[r];
-    uint64_t total;
-    uint64_t prefix = block_exclusive_scan_u64(local, wave_tot, &total);
-    const double target = (double)p * (double)total;
+    const double target = (double)p * (double)carry;
     const uint64_t tint = (uint64_t)ceil(target);
     int cnt = 0;
-    for (int r = r0; r < r1; ++r) {
-      prefix += keys[r];
-      cnt += (prefix < tint) ? 1 : 0;
-    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += (e * 64 + lane < nb && prefix[e] < tint) ? 1 : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-    if ((tid & 63) == 0) wave_cnt[tid >> 6] = cnt;
-    __syncthreads();
-    cnt = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
     kp = min(nb, cnt + 1);
   }
-  if (tid == 0) {
-    const int ki = max(kp, min(k_min, nb));
-    row_count[row] = ki;
-    atomicAdd(&head_count[h], ki);
-  }
+  return max(kp, min(k_min, nb));
 }
 
-// ---------------------------------------------------------------------------
-// Launch sequence for fva_route.
-// ---------------------------------------------------------------------------
+template <int E>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    const float* __restrict__ scores, int nb, int rows, float top_p, int k_min,
+    int16_t* __restrict__ ranked, int32_t* __restrict__ row_count,
+    int32_t* __restrict__ head_count) {
+  __shared__ int wg_sum;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int first = blockIdx.x * 4 * SEL_ROWS;
+  const int last = min(rows, first + 4 * SEL_ROWS) - 1;
+  const bool one_head = first / nb == last / nb;  // the common case: pool the workgroup's sum
+  if (threadIdx.x == 0) wg_sum = 0;
+  __syncthreads();
+  int head = -1, sum = 0;
+  for (int j = 0; j < SEL_ROWS; ++j) {
+    const int row = first + wave * SEL_ROWS + j;
+    if (row >= rows) break;  // uniform per wave
+    const int ki = select_row<E>(scores, nb, row, top_p, k_min, ranked, lane);
+    if (lane == 0) row_count[row] = ki;
+    const int h = row / nb;
+    if (h != head) {
+      if (head >= 0 && lane == 0) atomicAdd(&head_count[head], sum);
+      head = h;
+      sum = 0;
+    }
+    sum += ki;
+  }
+  if (head >= 0 && lane == 0) {
+    if (one_head) atomicAdd(&wg_sum, sum);
+    else atomicAdd(&head_count[head], sum);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && one_head) atomicAdd(&head_count[first / nb], wg_sum);
+}
+
 int launch_route(const fva_problem& p, int nb, const void* q, const void* k, const void* v,
                  float* scores, int16_t* ranked, int32_t* row_count,
                  int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
@@ -327,11 +375,18 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   st = record_hip_error(hipGetLastError(), "route_scores launch");
   if (st) return st;
 
-  int npad = 1;
-  while (npad < nb) npad <<= 1;
-  const dim3 sel_grid(nb, p.num_heads);
-  route_select_kernel<<<sel_grid, 256, 0, stream>>>(scores, nb, npad, p.top_p, p.k_min,
-                                                    ranked, row_count, head_count);
+  const int rows = p.num_heads * nb;
+  const int sel_grid = (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
+  int e = 1;
+  while (64 * e < nb) e <<= 1;
+  switch (e) {
+    case 1: route_select_kernel<1><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    case 2: route_select_kernel<2><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    case 4: route_select_kernel<4><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    case 8: route_select_kernel<8><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    case 16: route_select_kernel<16><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    default: route_select_kernel<32><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+  }
   return record_hip_error(hipGetLastError(), "route_select launch");
 }
 
