@@ -11,10 +11,11 @@ from .fva import (  # noqa: F401
     attn_workgroups,
     load_library,
     make_problem,
+    mfma_probe,
     plan,
     route,
     sizes,
     sparse_attn_fwd,
 )
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -41,6 +41,20 @@ static DeviceInfo g_dev[64];
 
 static int variant_index(int d, int block) { return (d == 128 ? 2 : 0) + (block == 128 ? 1 : 0); }
 
+// Compute units of the current device (cached), 0 on error.
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& info = g_dev[dev];
+  if (info.cus == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    info.cus = cus > 0 ? cus : 1;
+  }
+  return info.cus;
+}
+
 static int attn_grid(const fva_problem& p, int nb, int* grid) {
   int dev = 0;
   int st = record_hip_error(hipGetDevice(&dev), "hipGetDevice");

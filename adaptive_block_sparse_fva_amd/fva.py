@@ -34,6 +34,7 @@ EXPORTED = (
     "fva_route",
     "fva_plan",
     "fva_sparse_attn_fwd",
+    "fva_mfma_probe",
     "fva_status_string",
     "fva_last_error",
     "fva_version",
@@ -103,13 +104,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+    lib.fva_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64,
+                                   ctypes.POINTER(ctypes.c_double), vp]
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
     lib.fva_last_error.argtypes = []
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
     for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
-                 "fva_sparse_attn_fwd", "fva_version"):
+                 "fva_sparse_attn_fwd", "fva_mfma_probe", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -191,6 +194,15 @@ def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta,
                                             workspace.numel() * workspace.element_size(),
                                             _stream(stream))
     _check(st, "fva_sparse_attn_fwd")
+
+
+def mfma_probe(iters: int, random_operands: bool, sink: torch.Tensor, stream=None) -> float:
+    """Enqueue the MFMA-rate diagnostic kernel; returns the FLOPs it performs."""
+    flops = ctypes.c_double(0.0)
+    st = load_library().fva_mfma_probe(int(iters), 1 if random_operands else 0, _ptr(sink),
+                                       sink.numel(), ctypes.byref(flops), _stream(stream))
+    _check(st, "fva_mfma_probe")
+    return float(flops.value)
 
 
 @dataclass

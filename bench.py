@@ -39,6 +39,9 @@ def parse():
                     help="wall-clock budget of the oracle's attention sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device to device three times (a known byte count for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -148,6 +151,17 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        n = 256 * 1024 * 1024  # float32: 1 GiB read and 1 GiB written per copy
+        x = torch.ones(n, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print("copied 1 GiB x 3", flush=True)
+        return
+
     import adaptive_block_sparse_fva_amd as F
     from synth import WORKLOADS, make_inputs
 
@@ -218,6 +232,21 @@ def main():
     natural = list_schedule_makespan(costs, workers)
     ideal = costs.sum() / workers
 
+    # the bf16 MFMA rate this device sustains with no memory traffic (its
+    # clock under MFMA load depends on the operand data): context for the
+    # roofline fraction against the nominal peak
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda")
+    ceiling = {}
+    for label, rnd in (("random_operands", True), ("zero_operands", False)):
+        F.mfma_probe(200, rnd, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flops = F.mfma_probe(20000, rnd, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ceiling[label] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
     dense = None
     if not args.skip_dense:
         dprob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, 1.0, wl.k_min, 0)
@@ -276,7 +305,10 @@ def main():
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if wl.name == "rank480p" else None,
                      "kernel": "sparse_attn_fwd_kernel<128,128,64,2>",
-                     "algorithmic_flops_per_launch": kept},
+                     "algorithmic_flops_per_launch": kept,
+                     "timed": "attention call = attention kernel + merge of split tiles",
+                     "sustained_mfma_tflops": ceiling,
+                     "frac_of_sustained": round(achieved_tflops / ceiling["random_operands"], 4)},
         "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
                          "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4)},

@@ -211,6 +211,22 @@ int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         void* o, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * Diagnostic (not part of the hot path): enqueue a kernel that runs only
+ * bf16 MFMAs (v_mfma_f32_32x32x16_bf16, four independent chains per wave,
+ * two 256-thread workgroups per compute unit) for `iters` rounds, with zero
+ * operands (random_operands = 0) or N(0,1)-like ones (1).  The caller times
+ * it on `stream`; *flops receives the FLOPs it performs.  The clock a device
+ * sustains under MFMA load depends on the operand data, so this gives the
+ * matrix-unit rate actually reachable with realistic data, next to the
+ * nominal peak.
+ *   sink         device float [sink_elems >= 512 * compute units], written.
+ * Returns FVA_ERR_ARG for iters < 1 or null pointers, FVA_ERR_WORKSPACE for a
+ * short sink.
+ */
+int fva_mfma_probe(int32_t iters, int32_t random_operands, float* sink,
+                   int64_t sink_elems, double* flops, void* stream);
+
 /* Static text for a status code. */
 const char* fva_status_string(int status);
 

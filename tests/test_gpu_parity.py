@@ -238,3 +238,16 @@ def test_kv_relayout_is_the_documented_permutation(name):
     cols = np.array([_vt_key(j) for j in range(64)])
     vt_ref = vp.reshape(H, npad // 64, 64, d)[:, :, cols, :].transpose(0, 1, 3, 2)
     np.testing.assert_array_equal(kv[1].reshape(H, npad // 64, d, 64), vt_ref)
+
+
+def test_mfma_probe_reports_a_rate():
+    """The MFMA-rate diagnostic runs and reports a plausible FLOP count."""
+    say("[gpu] mfma probe")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda")
+    flops = F.mfma_probe(10, True, sink)
+    torch.cuda.synchronize()
+    assert flops == 2 * cus * 4 * 10 * 4 * 32768
+    assert torch.isfinite(sink).all()
+    with pytest.raises(F.FvaError):
+        F.mfma_probe(10, True, sink[:16])
