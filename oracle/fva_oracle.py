@@ -25,7 +25,9 @@ Sources (page title, section):
          unselected key blocks; S5.3 block importance is normalised over the
          key blocks of a query block (sums to 1); A.4 Top-p takes the shortest
          descending prefix whose cumulative sum reaches p; A.6 token reordering
-         so that nearby space-time tokens share blocks.
+         so that nearby space-time tokens share blocks; S5.3/A.2 precise block
+         importance: the mean over a query block's queries of the attention
+         weight on each key block, normalised over the evaluated keys.
 
 Readings where the pages are silent (each also listed in the design notes):
   * ordering: frame-major, spatial tiles tile_h x tile_w in raster order,
@@ -294,6 +296,41 @@ def masked_attention(q, k, v, order, block, row_ptr, col_idx, sm_scale,
         o[h, qt] = (p @ v[h, kt]) / l
         lse[h, qt] = (m + np.log(l))[:, 0]
     return o, lse
+
+
+def precise_block_importance(q, k, order, block, row_ptr, col_idx, sm_scale,
+                             tiles: Optional[Sequence[int]] = None):
+    """[GSRS] S5.3, A.2: the importance of key block j for query block i is the
+    attention weight the block's queries give to j's keys, averaged over those
+    queries, with the softmax taken over the keys actually evaluated (the row's
+    kept blocks); it sums to 1 over the kept blocks of each row.
+
+    Written out from that definition: per tile the full probability matrix of
+    its queries over its kept keys, summed over each kept block's keys,
+    averaged over the queries.  Returns fp64 [H][nb][nb] (0 for blocks not
+    kept; NaN rows outside the requested tiles).
+    """
+    H, N, d = q.shape
+    nb = num_blocks(N, block)
+    out = np.zeros((H, nb, nb))
+    todo = range(H * nb) if tiles is None else tiles
+    if tiles is not None:
+        out[:] = np.nan
+    for t in todo:
+        h, i = divmod(int(t), nb)
+        qt = _tile_tokens(order, block, i)
+        cols = [int(j) for j in col_idx[row_ptr[t]: row_ptr[t + 1]]]
+        toks = [_tile_tokens(order, block, j) for j in cols]
+        kt = np.concatenate(toks)
+        logits = sm_scale * (q[h, qt] @ k[h, kt].T)
+        prob = np.exp(logits - logits.max(axis=1, keepdims=True))
+        prob /= prob.sum(axis=1, keepdims=True)
+        out[h, i] = 0.0
+        start = 0
+        for j, tk in zip(cols, toks):
+            out[h, i, j] = prob[:, start: start + len(tk)].sum(axis=1).mean()
+            start += len(tk)
+    return out
 
 
 def dense_attention(q, k, v, sm_scale, rows: Optional[np.ndarray] = None, chunk: int = 2048):

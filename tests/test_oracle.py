@@ -336,6 +336,54 @@ def test_work_items_invariants():
         assert length.max() <= max(mean, (kept.max() + 1) // 2)
 
 
+def _tiny_routing(seed, H=2, grid=(2, 8, 8), block=32, d=16, p=0.6, k_min=1):
+    rng = np.random.default_rng(seed)
+    N = grid[0] * grid[1] * grid[2]
+    q, k = rng.standard_normal((H, N, d)), rng.standard_normal((H, N, d))
+    order = O.token_order(grid, (4, 8))
+    S = O.block_scores(O.pool(q, order, block), O.pool(k, order, block), 1 / math.sqrt(d)).astype(np.float32)
+    rc, _ = O.select_counts(S, p, k_min)
+    pl = O.plan(S, rc, 0)
+    return q, k, order, block, d, pl
+
+
+def test_precise_importance_rows_sum_to_one_over_kept_blocks():
+    q, k, order, block, d, pl = _tiny_routing(3)
+    imp = O.precise_block_importance(q, k, order, block, pl["row_ptr"], pl["col_idx"], 1 / math.sqrt(d))
+    H, nb, _ = imp.shape
+    np.testing.assert_allclose(imp.sum(axis=2), 1.0, atol=1e-12)
+    for t in range(H * nb):
+        h, i = divmod(t, nb)
+        kept = set(pl["col_idx"][pl["row_ptr"][t]: pl["row_ptr"][t + 1]].tolist())
+        for j in range(nb):
+            assert (imp[h, i, j] > 0) == (j in kept)
+
+
+def test_precise_importance_matches_torch_dense_probabilities():
+    # with every block kept, the importance is the block average of the dense
+    # attention map (torch's softmax, independent of the oracle's arithmetic)
+    import torch
+    rng = np.random.default_rng(4)
+    H, grid, block, d = 1, (1, 8, 12), 16, 8
+    N = grid[0] * grid[1] * grid[2]
+    q, k = rng.standard_normal((H, N, d)), rng.standard_normal((H, N, d))
+    order = O.token_order(grid, (0, 0))
+    nb = O.num_blocks(N, block)
+    row_ptr = np.arange(nb + 1) * nb
+    col_idx = np.tile(np.arange(nb), nb)
+    imp = O.precise_block_importance(q, k, order, block, row_ptr, col_idx, 0.3)
+    P = torch.softmax(0.3 * torch.from_numpy(q[0]) @ torch.from_numpy(k[0]).T, dim=1).numpy()
+    ref = P.reshape(nb, block, nb, block).sum(axis=3).mean(axis=1)
+    np.testing.assert_allclose(imp[0], ref, atol=1e-12)
+
+
+def test_precise_importance_single_kept_block_is_one():
+    q, k, order, block, d, pl = _tiny_routing(5, p=0.0, k_min=1)
+    imp = O.precise_block_importance(q, k, order, block, pl["row_ptr"], pl["col_idx"], 1 / math.sqrt(d))
+    assert np.all(np.diff(pl["row_ptr"]) == 1)
+    np.testing.assert_allclose(imp.max(axis=2), 1.0, atol=1e-12)
+
+
 def test_eq1_eq2_hand_examples():
     np.testing.assert_allclose(O.head_workload(np.array([32, 8]), 16), [2.0, 0.5])
     assert O.imbalance([3, 1, 1, 3]) == pytest.approx(1.5)
