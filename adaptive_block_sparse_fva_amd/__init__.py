@@ -9,6 +9,7 @@ from .fva import (  # noqa: F401
     FvaError,
     Problem,
     attn_workgroups,
+    block_importance,
     load_library,
     make_problem,
     mfma_probe,

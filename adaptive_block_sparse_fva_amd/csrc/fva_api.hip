@@ -20,7 +20,11 @@ int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                 const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
-                void* o, float* lse, void* workspace, float sm_scale, hipStream_t stream);
+                void* o, float* lse, float* block_lse, void* workspace, float sm_scale,
+                hipStream_t stream);
+int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* lse, const float* block_lse,
+                            float* importance, hipStream_t stream);
 int attn_blocks_per_cu(int d, int block);
 
 static thread_local char g_last_error[256] = "";
@@ -175,6 +179,7 @@ int fva_sizes(const fva_problem* prob, fva_sizes_t* out) {
   out->work_order_elems = rows + max_splits(prob, nb);
   out->plan_meta_elems = 2 + rows + FVA_MAX_SPLITS;
   out->attn_workspace_bytes = attn_workspace_need(prob, nb);
+  out->block_lse_capacity = rows * nb * prob->block;
   return FVA_OK;
 }
 
@@ -228,8 +233,8 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_
 int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                         const int32_t* work_order, const int32_t* plan_meta,
-                        uint32_t* tile_counter, void* o, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        uint32_t* tile_counter, void* o, float* lse, float* block_lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
@@ -240,11 +245,24 @@ int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
       !aligned16(workspace))
     return FVA_ERR_ARG;
   if ((int64_t)workspace_bytes < attn_workspace_need(prob, nb)) return FVA_ERR_WORKSPACE;
+  if (block_lse != nullptr && lse == nullptr) return FVA_ERR_ARG;
   int grid = 0;
   st = attn_grid(*prob, nb, &grid);
   if (st) return st;
   return launch_attn(*prob, nb, grid, q, kv, order, row_ptr, col_idx, work_order, plan_meta,
-                     tile_counter, o, lse, workspace, effective_scale(prob), (hipStream_t)stream);
+                     tile_counter, o, lse, block_lse, workspace, effective_scale(prob),
+                     (hipStream_t)stream);
+}
+
+int fva_block_importance(const fva_problem* prob, const int32_t* order, const int32_t* row_ptr,
+                         const int32_t* col_idx, const float* lse, const float* block_lse,
+                         float* importance, void* stream) {
+  int nb = 0;
+  int st = check_problem(prob, &nb);
+  if (st) return st;
+  if (!order || !row_ptr || !col_idx || !lse || !block_lse || !importance) return FVA_ERR_ARG;
+  return launch_block_importance(*prob, nb, order, row_ptr, col_idx, lse, block_lse, importance,
+                                 (hipStream_t)stream);
 }
 
 }  // extern "C"

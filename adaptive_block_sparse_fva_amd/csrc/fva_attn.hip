@@ -46,6 +46,7 @@ struct AttnArgs {
   const bf16_t* vt;  // [H][npad/64][d][64], V^T per 64-position sub-block
   bf16_t* o;
   float* lse;
+  float* block_lse;  // optional: per kept (row, block) pair, B per-query block LSEs
   const int32_t* order;
   const int32_t* row_ptr;
   const int32_t* col_idx;
@@ -215,6 +216,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    float blk_l = 0.f;  // this lane's share of the current key block's denominator
 
     // Per-lane LDS operand offsets (elements).  The swizzle depends on the row
     // modulo 16 only, which is the same for every 32-key sub-tile (K) and
@@ -342,6 +344,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        blk_l *= alpha;
 #pragma unroll
         for (int d = 0; d < DO; ++d)
 #pragma unroll
@@ -357,6 +360,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
           rs += p;
         }
       l_run += rs;
+      blk_l += rs;
 
       // ---- O^T += V^T P^T; the V^T operand of k-step ps and row tile d is
       // one 16-byte LDS load ----
@@ -385,12 +389,26 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
 
+      // GSRS S5.3 phase 1: after the last sub-block of a kept key block,
+      // each query's log-sum-exp over that block's keys (natural log, same
+      // scale as the row LSE); normalised by the final row LSE later
+      const bool rec = a.block_lse != nullptr && (u % SUB) == SUB - 1;
+      float blk_lse = 0.f;
+      if (rec) {
+        const float tot = blk_l + __shfl_xor(blk_l, 32, 64);
+        blk_lse = (m_run + __log2f(tot)) * 0.69314718055994531f;
+        blk_l = 0.f;
+      }
+
       // Sub-block u+1 has landed for every wave and every wave is done with
       // slot CUR.  In steady state the loads issued in the last NBUF-2 steps
       // may stay in flight; near the end wait for everything.
       if (u + NBUF < nsub) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * (NI + NIV)));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      // stored after the wait, so that the store completes behind the next
+      // sub-block's work instead of stalling this one
+      if (rec && hf == 0) a.block_lse[(int64_t)(c0 + u / SUB) * BLK + wave * 32 + l32] = blk_lse;
     };
     for (int u = 0; u < nsub; u += NBUF) {
       step(std::integral_constant<int, 0>{}, u);
@@ -511,6 +529,58 @@ int attn_blocks_per_cu(int d, int block) {
   return b < 1 ? 1 : b;
 }
 
+// GSRS S5.3 phase 2 (one workgroup per (head, query block) row): the
+// importance of kept block j is the mean over the block's queries of
+// exp(block LSE - row LSE), the share of each query's attention weight that
+// falls on j's keys; blocks not kept get 0.  Rows sum to 1.
+template <int BLK>
+__global__ __launch_bounds__(256) void block_importance_kernel(const int32_t* __restrict__ order,
+                                                              const int32_t* __restrict__ row_ptr,
+                                                              const int32_t* __restrict__ col_idx,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ block_lse, int n, int nb,
+                                                              float* __restrict__ importance) {
+  // The row's block LSEs are one contiguous run of (kept pairs) x BLK floats;
+  // the workgroup streams it with 16-byte loads, BLK/4 lanes per pair, and
+  // reduces each pair inside its lane group.
+  constexpr int LPP = BLK / 4;          // lanes per pair
+  constexpr int PPI = 256 / LPP;        // pairs per pass
+  __shared__ float row_lse[BLK];
+  const int t = blockIdx.x, h = t / nb, i = t - h * nb;
+  const int tid = threadIdx.x;
+  for (int qq = tid; qq < BLK; qq += 256) {
+    const int tok = order[i * BLK + qq];
+    row_lse[qq] = tok >= 0 ? lse[(int64_t)h * n + tok] : INFINITY;  // exp(x - inf) = 0 for slots past N
+  }
+  float* out = importance + (int64_t)t * nb;
+  for (int j = tid; j < nb; j += 256) out[j] = 0.f;
+  __syncthreads();
+  const float inv_rows = 1.0f / (float)min(BLK, n - i * BLK);
+  const int c0 = row_ptr[t], c1 = row_ptr[t + 1];
+  const int g = tid / LPP, r = (tid % LPP) * 4;
+  for (int c = c0 + g; c < c1; c += PPI) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(block_lse + (int64_t)c * BLK + r);
+    float acc = expf(x[0] - row_lse[r]) + expf(x[1] - row_lse[r + 1]) + expf(x[2] - row_lse[r + 2]) +
+                expf(x[3] - row_lse[r + 3]);
+#pragma unroll
+    for (int off = LPP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (tid % LPP == 0) out[col_idx[c]] = acc * inv_rows;
+  }
+}
+
+int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* lse, const float* block_lse,
+                            float* importance, hipStream_t stream) {
+  const int rows = p.num_heads * nb;
+  if (p.block == 128)
+    block_importance_kernel<128><<<rows, 256, 0, stream>>>(order, row_ptr, col_idx, lse, block_lse, p.seq_len, nb,
+                                                           importance);
+  else
+    block_importance_kernel<64><<<rows, 256, 0, stream>>>(order, row_ptr, col_idx, lse, block_lse, p.seq_len, nb,
+                                                          importance);
+  return record_hip_error(hipGetLastError(), "block_importance launch");
+}
+
 template <int D, int BLK>
 static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
   const int grid = rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
@@ -523,7 +593,8 @@ static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                 const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
-                void* o, float* lse, void* workspace, float sm_scale, hipStream_t stream) {
+                void* o, float* lse, float* block_lse, void* workspace, float sm_scale,
+                hipStream_t stream) {
   const int npad = nb * p.block;
   const bf16_t* kp = (const bf16_t*)kv;
   const bf16_t* vt = kp + (int64_t)p.num_heads * npad * p.head_dim;
@@ -534,6 +605,7 @@ int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const voi
   a.npad = npad;
   a.o = (bf16_t*)o;
   a.lse = lse;
+  a.block_lse = block_lse;
   a.order = order;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;

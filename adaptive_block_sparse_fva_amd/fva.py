@@ -34,6 +34,7 @@ EXPORTED = (
     "fva_route",
     "fva_plan",
     "fva_sparse_attn_fwd",
+    "fva_block_importance",
     "fva_mfma_probe",
     "fva_status_string",
     "fva_last_error",
@@ -81,6 +82,7 @@ class Sizes(ctypes.Structure):
         ("work_order_elems", ctypes.c_int64),
         ("plan_meta_elems", ctypes.c_int64),
         ("attn_workspace_bytes", ctypes.c_int64),
+        ("block_lse_capacity", ctypes.c_int64),
     ]
 
 
@@ -102,8 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+    lib.fva_block_importance.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64,
                                    ctypes.POINTER(ctypes.c_double), vp]
     lib.fva_status_string.argtypes = [ctypes.c_int]
@@ -112,7 +115,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
     for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
-                 "fva_sparse_attn_fwd", "fva_mfma_probe", "fva_version"):
+                 "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -186,14 +189,21 @@ def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, work_order
 
 
 def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta, tile_counter, o,
-                    workspace, lse=None, stream=None):
+                    workspace, lse=None, block_lse=None, stream=None):
     st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(kv), _ptr(order),
                                             _ptr(row_ptr), _ptr(col_idx), _ptr(work_order),
                                             _ptr(plan_meta), _ptr(tile_counter), _ptr(o),
-                                            _ptr(lse), _ptr(workspace),
+                                            _ptr(lse), _ptr(block_lse), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _stream(stream))
     _check(st, "fva_sparse_attn_fwd")
+
+
+def block_importance(prob, order, row_ptr, col_idx, lse, block_lse, importance, stream=None):
+    st = load_library().fva_block_importance(ctypes.byref(prob), _ptr(order), _ptr(row_ptr),
+                                             _ptr(col_idx), _ptr(lse), _ptr(block_lse),
+                                             _ptr(importance), _stream(stream))
+    _check(st, "fva_block_importance")
 
 
 def mfma_probe(iters: int, random_operands: bool, sink: torch.Tensor, stream=None) -> float:
@@ -264,13 +274,23 @@ class Buffers:
         plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
              self.head_count_final, self.work_order, self.plan_meta, self.tile_counter, stream)
 
-    def attn(self, q, work_order=None, with_lse=True, stream=None):
+    def attn(self, q, work_order=None, with_lse=True, block_lse=None, stream=None):
         """Attention over the K/V that the last route() call re-laid out, the
-        work items taken in the plan's order (or in work_order's)."""
+        work items taken in the plan's order (or in work_order's); block_lse
+        (float, >= row_ptr[-1] * B elements) also records per-block LSEs."""
         sparse_attn_fwd(self.prob, q, self.kv, self.order, self.row_ptr, self.col_idx,
                         self.work_order if work_order is None else work_order, self.plan_meta,
                         self.tile_counter, self.o, self.attn_workspace,
-                        self.lse if with_lse else None, stream)
+                        self.lse if with_lse else None, block_lse, stream)
+
+    def importance(self, block_lse, out=None, stream=None):
+        """Precise block importance [H][nb][nb] from the last attn(block_lse=...)."""
+        H = self.prob.num_heads
+        if out is None:
+            out = torch.empty((H, self.nb, self.nb), dtype=torch.float32, device=self.lse.device)
+        block_importance(self.prob, self.order, self.row_ptr, self.col_idx, self.lse, block_lse, out,
+                         stream)
+        return out
 
     def run(self, q, k, v, stream=None):
         """One full call of the hot path: route -> plan -> attention."""

@@ -232,6 +232,30 @@ def main():
     natural = list_schedule_makespan(costs, workers)
     ideal = costs.sum() / workers
 
+    # GSRS precise block importance (phase 1 inside the attention call, phase
+    # 2 as its own kernel): cost over the plain attention call
+    nnz = int(row_ptr[-1])
+    block_lse = torch.empty(nnz * B, dtype=torch.float32, device="cuda")
+    imp = torch.empty((H, nb, nb), dtype=torch.float32, device="cuda")
+    buf.attn(q, block_lse=block_lse)
+    buf.importance(block_lse, imp)
+    torch.cuda.synchronize()
+    n_imp = 10
+    ev_i = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev_i[0].record(stream)
+    for _ in range(n_imp):
+        buf.attn(q, block_lse=block_lse)
+    ev_i[1].record(stream)
+    for _ in range(n_imp):
+        buf.importance(block_lse, imp)
+    ev_i[2].record(stream)
+    torch.cuda.synchronize()
+    attn_lse_ms = ev_i[0].elapsed_time(ev_i[1]) / n_imp
+    imp_ms = ev_i[1].elapsed_time(ev_i[2]) / n_imp
+    precise = {"attn_with_block_lse_ms": round(attn_lse_ms, 4), "importance_kernel_ms": round(imp_ms, 4),
+               "overhead_vs_attn": round((attn_lse_ms + imp_ms) / attn_avg_ms - 1.0, 4),
+               "block_lse_bytes": nnz * B * 4}
+
     # the bf16 MFMA rate this device sustains with no memory traffic (its
     # clock under MFMA load depends on the operand data): context for the
     # roofline fraction against the nominal peak
@@ -309,6 +333,7 @@ def main():
                      "timed": "attention call = attention kernel + merge of split tiles",
                      "sustained_mfma_tflops": ceiling,
                      "frac_of_sustained": round(achieved_tflops / ceiling["random_operands"], 4)},
+        "precise_importance": precise,
         "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
                          "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4)},

@@ -102,6 +102,8 @@ typedef struct fva_sizes_t {
   int64_t work_order_elems;  /* H*nb + min(H*nb, FVA_MAX_SPLITS) int32 (work_order) */
   int64_t plan_meta_elems;   /* 2 + H*nb + FVA_MAX_SPLITS int32 (plan_meta) */
   int64_t attn_workspace_bytes; /* fva_sparse_attn_fwd workspace */
+  int64_t block_lse_capacity;/* H*nb*nb*B float: block_lse for any mask
+                                (row_ptr[H*nb] * B suffices for a given one) */
 } fva_sizes_t;
 
 /* Host only: validate a problem and report buffer sizes.  Makes no HIP call. */
@@ -199,6 +201,12 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
  *   o            device bf16 [H][N][d] (strided like q), written.
  *   lse          device float [H][N] or NULL, written: natural-log
  *                log-sum-exp of each query's kept logits.
+ *   block_lse    device float [row_ptr[H*nb] * B] or NULL (requires lse),
+ *                written: GSRS S5.3 phase 1, for kept pair c of the CSR mask
+ *                (row t, key block col_idx[c]) and query slot r of the row's
+ *                query block (position t%nb * B + r), the natural-log
+ *                log-sum-exp of that query's logits over the block's keys, at
+ *                [c * B + r].  Slots past N hold unspecified values.
  *   workspace    device scratch of workspace_bytes >=
  *                fva_sizes().attn_workspace_bytes, 16-byte aligned: the
  *                partial results of split tiles; contents are not needed
@@ -208,8 +216,23 @@ int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* order, const int32_t* row_ptr,
                         const int32_t* col_idx, const int32_t* work_order,
                         const int32_t* plan_meta, uint32_t* tile_counter,
-                        void* o, float* lse, void* workspace,
+                        void* o, float* lse, float* block_lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Precise block importance (GSRS S5.3 phase 2, A.2): after an attention call
+ * that recorded block_lse and lse, the importance of kept key block j for
+ * query block i of head h is the mean over the block's queries of
+ * exp(block LSE - row LSE), i.e. the average share of a query's attention
+ * weight (softmax over the row's kept keys) that falls on j; it sums to 1
+ * over the row's kept blocks.
+ *   order, row_ptr, col_idx, lse, block_lse   as used / written above.
+ *   importance   device float [H][nb][nb], written (0 for blocks not kept).
+ */
+int fva_block_importance(const fva_problem* prob, const int32_t* order,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const float* lse, const float* block_lse,
+                         float* importance, void* stream);
 
 /*
  * Diagnostic (not part of the hot path): enqueue a kernel that runs only

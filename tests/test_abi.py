@@ -112,7 +112,9 @@ def test_entry_points_reject_null_pointers_without_a_device():
     assert st == fva.FVA_ERR_ARG
     st = lib.fva_plan(ctypes.byref(p), *([null] * 9))
     assert st == fva.FVA_ERR_ARG
-    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 11), 0, null)
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 12), 0, null)
+    assert st == fva.FVA_ERR_ARG
+    st = lib.fva_block_importance(ctypes.byref(p), *([null] * 7))
     assert st == fva.FVA_ERR_ARG
     assert lib.fva_sizes(None, None) == fva.FVA_ERR_ARG
     assert lib.fva_status_string(fva.FVA_ERR_WORKSPACE) == b"workspace too small"
@@ -155,8 +157,9 @@ def test_attention_argument_checks_before_launch():
     mis = ctypes.c_void_p((1 << 20) + 8)
 
     def call(kv=fake, ws=fake, nbytes=need):
-        # q kv order row_ptr col_idx work_order plan_meta tile_counter o lse workspace bytes stream
-        return lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, kv, *([fake] * 6), fake, None, ws,
+        # q kv order row_ptr col_idx work_order plan_meta tile_counter o lse block_lse workspace
+        # bytes stream
+        return lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, kv, *([fake] * 6), fake, None, None, ws,
                                        nbytes, None)
 
     assert call(kv=mis) == fva.FVA_ERR_ARG
@@ -164,6 +167,10 @@ def test_attention_argument_checks_before_launch():
     assert call(ws=mis) == fva.FVA_ERR_ARG
     assert call(ws=None) == fva.FVA_ERR_ARG
     assert call(nbytes=need - 1) == fva.FVA_ERR_WORKSPACE
+    # block LSEs need the row LSEs they are normalised by
+    st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, fake, *([fake] * 6), fake, None, fake, fake,
+                                 need, None)
+    assert st == fva.FVA_ERR_ARG
 
 
 def test_binding_refuses_cpu_tensors():

@@ -251,3 +251,45 @@ def test_mfma_probe_reports_a_rate():
     assert torch.isfinite(sink).all()
     with pytest.raises(F.FvaError):
         F.mfma_probe(10, True, sink[:16])
+
+
+IMPORTANCE_ABS = 1e-4  # fp32 exponentials and sums of at most B keys vs fp64
+
+
+@pytest.mark.parametrize("name,refill", [("two_head", 0), ("rank480p", 0), ("edge_ragged_split", 250)])
+def test_precise_block_importance_matches_oracle(name, refill):
+    """GSRS S5.3: per-block LSE recorded in the attention kernel, normalised by
+    the row LSE afterwards, against the oracle's mean attention weight per kept
+    block."""
+    if name == "edge_ragged_split":
+        wl = Workload(name, 2, 128, (3, 9, 11), 64, (0.8,), 1, refill, seed=13, heads="conc_flat",
+                      tile=(8, 8))
+        inp = make_inputs(wl, cache=False)
+    else:
+        wl = WORKLOADS[name]
+        inp = make_inputs(wl)
+    say(f"[gpu] precise importance {name}")
+    q, k, v = device_inputs(inp)
+    prob = problem_for(wl, wl.top_p[0], refill)
+    buf = F.Buffers.allocate(prob)
+    buf.route(q, k, v)
+    buf.plan()
+    torch.cuda.synchronize()
+    nnz = int(buf.row_ptr[-1].item())
+    block_lse = torch.empty(nnz * wl.block, dtype=torch.float32, device="cuda")
+    buf.attn(q, block_lse=block_lse)
+    imp = buf.importance(block_lse)
+    torch.cuda.synchronize()
+    got = imp.cpu().numpy().astype(np.float64)
+    res = gpu_host = __import__("gpu_helpers").host(buf)
+    H, nb = wl.num_heads, res["nb"]
+    np.testing.assert_allclose(got.sum(axis=2), 1.0, atol=IMPORTANCE_ABS)
+    q64, k64, _ = f64_inputs(inp)
+    order = O.token_order(wl.grid, wl.tile_hw)
+    tiles = None if H * nb <= 256 else sample_tiles(res["row_ptr"], H, nb, per_head=10, seed=3)
+    ref = O.precise_block_importance(q64, k64, order, wl.block, res["row_ptr"], res["col_idx"],
+                                     1.0 / math.sqrt(wl.head_dim), tiles)
+    rows = [divmod(int(t), nb) for t in (range(H * nb) if tiles is None else tiles)]
+    err = max(np.abs(got[h, i] - ref[h, i]).max() for h, i in rows)
+    say(f"  importance max-abs {err:.2e} over {len(rows)} rows; split tiles {int(res['plan_meta'][1])}")
+    assert err <= IMPORTANCE_ABS
