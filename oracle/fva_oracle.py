@@ -104,6 +104,62 @@ def token_order(grid: Tuple[int, int, int], tile: Tuple[int, int]) -> np.ndarray
     return np.asarray(out, dtype=np.int64)
 
 
+def _hilbert_walk(o, da, db, w, h, out):
+    """Append the cells o + i*da + j*db (0 <= i < w along the primary vector da,
+    0 <= j < h along the secondary db) in generalised Hilbert order, starting
+    at o and, except in the single-column case, ending at o + (w-1)*da."""
+    if h == 1:
+        for i in range(w):
+            out.append((o[0] + i * da[0], o[1] + i * da[1]))
+        return
+    if w == 1:
+        for j in range(h):
+            out.append((o[0] + j * db[0], o[1] + j * db[1]))
+        return
+    if w > 2 * h:
+        # long along the primary: two halves walked one after the other
+        w0 = (w + 1) // 2
+        _hilbert_walk(o, da, db, w0, h, out)
+        _hilbert_walk((o[0] + w0 * da[0], o[1] + w0 * da[1]), da, db, w - w0, h, out)
+        return
+    if h > 2 * w:
+        # long along the secondary: up over the first ceil(w/2) columns, then
+        # down over the rest from the far corner, ending at o + (w-1)*da
+        w0 = (w + 1) // 2
+        _hilbert_walk(o, db, da, h, w0, out)
+        o1 = (o[0] + (w - 1) * da[0] + (h - 1) * db[0], o[1] + (w - 1) * da[1] + (h - 1) * db[1])
+        _hilbert_walk(o1, (-db[0], -db[1]), (-da[0], -da[1]), h, w - w0, out)
+        return
+    # the four quadrants in Hilbert's U: first one transposed, last one
+    # transposed and reversed, so every quadrant starts next to the previous end
+    w0, h0 = (w + 1) // 2, (h + 1) // 2
+    w1, h1 = w - w0, h - h0
+    _hilbert_walk(o, db, da, h0, w0, out)
+    o1 = (o[0] + h0 * db[0], o[1] + h0 * db[1])
+    _hilbert_walk(o1, da, db, w0, h1, out)
+    _hilbert_walk((o1[0] + w0 * da[0], o1[1] + w0 * da[1]), da, db, w1, h1, out)
+    o3 = (o[0] + (w - 1) * da[0] + (h0 - 1) * db[0], o[1] + (w - 1) * da[1] + (h0 - 1) * db[1])
+    _hilbert_walk(o3, (-db[0], -db[1]), (-da[0], -da[1]), h0, w1, out)
+
+
+def hilbert_order(grid: Tuple[int, int, int]) -> np.ndarray:
+    """pi for the Hilbert-curve reordering ([FVA] S3.1, [GSRS] A.6), by explicit
+    enumeration: frames in time order; inside a frame the grid_h x grid_w
+    cells along a generalised Hilbert curve that starts at (x, y) = (0, 0)
+    with its primary direction along x.  The generalisation to any width w
+    (along the primary) and height h: a strip of height 1 (or width 1) is
+    walked straight; if w > 2h the two halves of the primary are walked one
+    after the other; if h > 2w the first ceil(w/2) columns are walked up and
+    the others down from the far corner; otherwise the four quadrants (first
+    ceil(w/2) columns, first ceil(h/2) rows) are visited as in Hilbert's
+    curve.  For 2^k x 2^k frames this is Hilbert's curve itself."""
+    T, H, W = grid
+    cells = []
+    _hilbert_walk((0, 0), (1, 0), (0, 1), W, H, cells)
+    frame = np.array([y * W + x for x, y in cells], dtype=np.int64)
+    return np.concatenate([t * H * W + frame for t in range(T)])
+
+
 def padded_order(order: np.ndarray, block: int) -> np.ndarray:
     """The order as nb*B slots, -1 in the slots past the end of the sequence."""
     nb = num_blocks(len(order), block)

@@ -384,6 +384,55 @@ def test_precise_importance_single_kept_block_is_one():
     np.testing.assert_allclose(imp.max(axis=2), 1.0, atol=1e-12)
 
 
+def _textbook_hilbert_d2xy(n, d):
+    # the classic bit-by-bit index -> point conversion of Hilbert's curve on an
+    # n x n grid (n a power of two)
+    x = y = 0
+    s, t = 1, d
+    while s < n:
+        rx = 1 & (t // 2)
+        ry = 1 & (t ^ rx)
+        if ry == 0:
+            if rx == 1:
+                x, y = s - 1 - x, s - 1 - y
+            x, y = y, x
+        x += s * rx
+        y += s * ry
+        t //= 4
+        s *= 2
+    return x, y
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32])
+def test_hilbert_order_is_the_textbook_curve_on_power_of_two_squares(n):
+    order = O.hilbert_order((1, n, n))
+    ref = [_textbook_hilbert_d2xy(n, d) for d in range(n * n)]
+    np.testing.assert_array_equal(order, [y * n + x for x, y in ref])
+
+
+@pytest.mark.parametrize("grid", [(1, 30, 52), (2, 45, 80), (1, 55, 64), (3, 5, 7), (1, 1, 9), (1, 9, 1),
+                                  (1, 2, 13), (1, 13, 2), (1, 3, 3)])
+def test_hilbert_order_is_a_local_permutation(grid):
+    T, H, W = grid
+    order = O.hilbert_order(grid)
+    np.testing.assert_array_equal(np.sort(order), np.arange(T * H * W))
+    # frame-major, and inside a frame almost every step moves to a grid neighbour
+    frame = order[: H * W]
+    assert np.all(order.reshape(T, H * W) - np.arange(T)[:, None] * H * W == frame)
+    y, x = frame // W, frame % W
+    step = np.abs(np.diff(y)) + np.abs(np.diff(x))
+    assert step[0] <= 1 if len(step) else True
+    assert np.mean(step <= 2) >= 0.95
+    if min(H, W) >= 8:
+        assert np.mean(step == 1) >= 0.85
+    # 128-token blocks are compact: their bounding boxes have about half the
+    # height + width of the thin full-width strips that raster order gives
+    if H * W >= 1024:
+        hw = [np.ptp(y[i:i + 128]) + np.ptp(x[i:i + 128]) + 2 for i in range(0, H * W - 127, 128)]
+        raster = [np.ptp(np.arange(i, i + 128) // W) + 1 + min(W, 128) for i in range(0, H * W - 127, 128)]
+        assert np.mean(hw) < 0.6 * np.mean(raster)
+
+
 def test_eq1_eq2_hand_examples():
     np.testing.assert_allclose(O.head_workload(np.array([32, 8]), 16), [2.0, 0.5])
     assert O.imbalance([3, 1, 1, 3]) == pytest.approx(1.5)
