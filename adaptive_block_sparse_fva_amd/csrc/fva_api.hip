@@ -95,6 +95,8 @@ static int check_problem(const fva_problem* p, int* nb_out) {
   if (p->grid_t < 1 || p->grid_h < 1 || p->grid_w < 1) return FVA_ERR_ARG;
   if ((int64_t)p->grid_t * p->grid_h * p->grid_w != (int64_t)p->seq_len) return FVA_ERR_ARG;
   if (p->tile_h < 0 || p->tile_w < 0) return FVA_ERR_ARG;
+  if (p->order_kind != FVA_ORDER_TILES && p->order_kind != FVA_ORDER_HILBERT) return FVA_ERR_ARG;
+  if (p->reserved != 0) return FVA_ERR_ARG;
   if ((p->tile_h == 0) != (p->tile_w == 0)) return FVA_ERR_ARG;
   if (isnan(p->top_p)) return FVA_ERR_ARG;
   if (p->k_min < 1) return FVA_ERR_ARG;

@@ -39,6 +39,7 @@ struct FastDiv {
 // into tile_h x tile_w spatial tiles (raster order of tiles, raster inside a
 // tile, tiles cut at the frame border).  Position -> natural token index.
 struct OrderGeo {
+  int32_t kind;                // FVA_ORDER_TILES or FVA_ORDER_HILBERT
   int32_t n, hw, gw, th, tw;   // tokens, grid_h*grid_w, grid_w, tile dims (0 = raster)
   int32_t gh;                  // grid_h
   FastDiv div_hw;              // by grid_h*grid_w
@@ -49,8 +50,71 @@ struct OrderGeo {
   FastDiv div_w_last;          // by last_w (short last tile column)
   int32_t last_h, last_w;      // height of the last band, width of the last tile column
 
+  // Cell d of a frame along the generalised Hilbert curve (the walk the
+  // header describes), found by descending its recursion: at each level the
+  // part holding d, with the part's origin and axes.
+  __device__ __forceinline__ int32_t hilbert_cell(int32_t d) const {
+    int32_t ox = 0, oy = 0, ax = 1, ay = 0, bx = 0, by = 1, w = gw, h = gh;
+    for (;;) {
+      if (h == 1) { ox += d * ax; oy += d * ay; break; }
+      if (w == 1) { ox += d * bx; oy += d * by; break; }
+      const int32_t w0 = (w + 1) >> 1;
+      if (w > 2 * h) {
+        if (d < w0 * h) {
+          w = w0;
+        } else {
+          d -= w0 * h;
+          ox += w0 * ax; oy += w0 * ay;
+          w -= w0;
+        }
+        continue;
+      }
+      int32_t t0;
+      if (h > 2 * w) {
+        if (d < h * w0) {
+          t0 = ax; ax = bx; bx = t0;
+          t0 = ay; ay = by; by = t0;
+          const int32_t nw = h; h = w0; w = nw;
+        } else {
+          d -= h * w0;
+          ox += (w - 1) * ax + (h - 1) * bx; oy += (w - 1) * ay + (h - 1) * by;
+          t0 = ax; ax = -bx; bx = -t0;
+          t0 = ay; ay = -by; by = -t0;
+          const int32_t nw = h; h = w - w0; w = nw;
+        }
+        continue;
+      }
+      const int32_t h0 = (h + 1) >> 1, w1 = w - w0, h1 = h - h0;
+      const int32_t s0 = h0 * w0, s1 = w0 * h1, s2 = w1 * h1;
+      if (d < s0) {
+        t0 = ax; ax = bx; bx = t0;
+        t0 = ay; ay = by; by = t0;
+        w = h0; h = w0;
+      } else if (d < s0 + s1) {
+        d -= s0;
+        ox += h0 * bx; oy += h0 * by;
+        w = w0; h = h1;
+      } else if (d < s0 + s1 + s2) {
+        d -= s0 + s1;
+        ox += h0 * bx + w0 * ax; oy += h0 * by + w0 * ay;
+        w = w1; h = h1;
+      } else {
+        d -= s0 + s1 + s2;
+        ox += (w - 1) * ax + (h0 - 1) * bx; oy += (w - 1) * ay + (h0 - 1) * by;
+        t0 = ax; ax = -bx; bx = -t0;
+        t0 = ay; ay = -by; by = -t0;
+        w = h0; h = w1;
+      }
+    }
+    return oy * gw + ox;
+  }
+
   __device__ __forceinline__ int32_t token(int32_t pos) const {
     if (pos >= n) return -1;
+    if (kind == FVA_ORDER_HILBERT) {
+      const uint32_t t = div_hw.div((uint32_t)pos);
+      return (int32_t)(t * (uint32_t)hw) + hilbert_cell(pos - (int32_t)(t * (uint32_t)hw));
+    }
     if (th == 0) return pos;
     const uint32_t t = div_hw.div((uint32_t)pos);
     const uint32_t r = (uint32_t)pos - t * (uint32_t)hw;
@@ -70,6 +134,7 @@ struct OrderGeo {
 
 inline OrderGeo make_order_geo(const fva_problem& p) {
   OrderGeo g;
+  g.kind = p.order_kind;
   g.n = p.seq_len;
   g.hw = p.grid_h * p.grid_w;
   g.gw = p.grid_w;

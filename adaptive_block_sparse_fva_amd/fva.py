@@ -27,6 +27,8 @@ FVA_ERR_WORKSPACE = 4
 FVA_MAX_BLOCKS = 2048
 FVA_MAX_TILES = 16384
 FVA_MAX_SPLITS = 1024
+FVA_ORDER_TILES = 0
+FVA_ORDER_HILBERT = 1
 
 EXPORTED = (
     "fva_sizes",
@@ -65,6 +67,8 @@ class Problem(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("stride_head", ctypes.c_int64),
         ("stride_token", ctypes.c_int64),
+        ("order_kind", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -133,15 +137,19 @@ def _check(status: int, where: str) -> None:
 def make_problem(num_heads: int, seq_len: int, head_dim: int, grid: Sequence[int], block: int,
                  tile: Sequence[int], top_p: float, k_min: int, refill_per_mille: int = 0,
                  sm_scale: float = 0.0, stride_head: Optional[int] = None,
-                 stride_token: Optional[int] = None) -> Problem:
-    """Problem struct; default strides describe contiguous [H][N][d] tensors."""
+                 stride_token: Optional[int] = None, order: str = "tiles") -> Problem:
+    """Problem struct; default strides describe contiguous [H][N][d] tensors;
+    order is "tiles" (frame-major spatial tiles) or "hilbert"."""
     if stride_token is None:
         stride_token = head_dim
     if stride_head is None:
         stride_head = seq_len * stride_token
+    kinds = {"tiles": FVA_ORDER_TILES, "hilbert": FVA_ORDER_HILBERT}
+    if order not in kinds:
+        raise FvaError(FVA_ERR_ARG, "make_problem", f"unknown order {order!r}")
     return Problem(num_heads, seq_len, head_dim, grid[0], grid[1], grid[2], block, tile[0],
                    tile[1], float(top_p), k_min, refill_per_mille, float(sm_scale), stride_head,
-                   stride_token)
+                   stride_token, kinds[order], 0)
 
 
 def sizes(prob: Problem) -> Sizes:

@@ -289,7 +289,33 @@ def main():
         dense = {"ms_per_call": round(dense_ms, 4),
                  "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1),
                  "sparse_speedup": round(dense_ms / ms_per_step, 3)}
+        lse_dense = dbuf.lse.clone()
         del dbuf
+
+        # token order (FVAttn S3.1 / GSRS A.6): the frame/tile order against the
+        # generalised Hilbert curve at the same p -- kept density, attention
+        # recall (share of each query's dense softmax mass on its kept keys)
+        # and time per call
+        def order_stats(b, ms):
+            rp = b.row_ptr.cpu().numpy().astype(np.int64)
+            recall = torch.exp(b.lse - lse_dense).mean().item()
+            return {"density": round(float(rp[-1]) / (H * nb * nb), 4), "recall": round(recall, 4),
+                    "ms_per_call": round(ms, 4)}
+        hprob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, p, wl.k_min, wl.refill_per_mille,
+                               order="hilbert")
+        hbuf = F.Buffers.allocate(hprob)
+        hbuf.run(q, k, v)
+        hbuf.run(q, k, v)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            hbuf.run(q, k, v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        order_cmp = {"tiles": order_stats(buf, ms_per_step),
+                     "hilbert": order_stats(hbuf, e0.elapsed_time(e1) / reps)}
+        dense["order_comparison"] = order_cmp
+        del hbuf
 
     cpu = None
     if not args.skip_cpu_baseline:

@@ -86,7 +86,30 @@ typedef struct fva_problem {
   float sm_scale;            /* softmax scale; 0 = 1/sqrt(d) */
   int64_t stride_head;       /* elements between heads in q, k, v, o */
   int64_t stride_token;      /* elements between tokens (>= d) */
+  int32_t order_kind;        /* FVA_ORDER_TILES (default) or FVA_ORDER_HILBERT */
+  int32_t reserved;          /* must be 0 */
 } fva_problem;
+
+/*
+ * Token orders (FVAttn S3.1, GSRS A.6; both frame-major):
+ *   FVA_ORDER_TILES    tile_h x tile_w spatial tiles in raster order, raster
+ *                      inside a tile, edge tiles cut at the border
+ *                      (tile_h = tile_w = 0: natural order);
+ *   FVA_ORDER_HILBERT  each frame along a generalised Hilbert curve from
+ *                      (x, y) = (0, 0), primary direction x (tile ignored):
+ *                      for a w x h rectangle walked from its origin along
+ *                      primary a, secondary b, a 1-high strip is walked along
+ *                      a and a 1-wide one along b; if w > 2h the two halves
+ *                      of a (first ceil(w/2)) are walked in turn; if h > 2w
+ *                      the first ceil(w/2) columns are walked with a and b
+ *                      swapped, then the rest from the far corner with both
+ *                      reversed; otherwise the quadrants (first ceil(w/2)
+ *                      columns, first ceil(h/2) rows) are walked in
+ *                      Hilbert's U (first transposed, last transposed and
+ *                      reversed).  For 2^k x 2^k frames: Hilbert's curve.
+ */
+#define FVA_ORDER_TILES 0
+#define FVA_ORDER_HILBERT 1
 
 /* Sizes derived from a problem (element counts unless named _bytes). */
 typedef struct fva_sizes_t {

@@ -173,6 +173,21 @@ def test_attention_argument_checks_before_launch():
     assert st == fva.FVA_ERR_ARG
 
 
+def test_order_kind_and_reserved_are_checked():
+    lib = F.load_library()
+    out = fva.Sizes()
+    for kind, want in ((fva.FVA_ORDER_TILES, fva.FVA_OK), (fva.FVA_ORDER_HILBERT, fva.FVA_OK),
+                       (2, fva.FVA_ERR_ARG), (-1, fva.FVA_ERR_ARG)):
+        p = _ok_problem()
+        p.order_kind = kind
+        assert lib.fva_sizes(ctypes.byref(p), ctypes.byref(out)) == want
+    p = _ok_problem()
+    p.reserved = 1
+    assert lib.fva_sizes(ctypes.byref(p), ctypes.byref(out)) == fva.FVA_ERR_ARG
+    with pytest.raises(F.FvaError):
+        F.make_problem(1, 1024, 64, (4, 16, 16), 64, (8, 8), 0.9, 1, order="zigzag")
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     p = _ok_problem(num_heads=1, seq_len=1024, head_dim=64, grid=(4, 16, 16), block=64, tile=(8, 8))

@@ -26,20 +26,20 @@ CASES = [(name, p) for name in WORKLOAD_ORDER for p in WORKLOADS[name].top_p]
 FULL_ATTENTION = {"tiny", "two_head"}
 
 
-def _oracle_scores(wl, inp):
+def _oracle_scores(wl, inp, order=None):
     q64, k64, _ = f64_inputs(inp)
-    order = O.token_order(wl.grid, wl.tile_hw)
+    order = O.token_order(wl.grid, wl.tile_hw) if order is None else order
     return O.block_scores(O.pool(q64, order, wl.block), O.pool(k64, order, wl.block),
                           1.0 / math.sqrt(wl.head_dim))
 
 
-def check_routing_and_plan(wl, inp, res, p, refill):
+def check_routing_and_plan(wl, inp, res, p, refill, order=None, kind="tiles"):
     H, nb = wl.num_heads, res["nb"]
+    order = O.token_order(wl.grid, wl.tile_hw) if order is None else order
     # order: closed form on the GPU vs enumeration in the oracle
-    np.testing.assert_array_equal(
-        res["order"], O.padded_order(O.token_order(wl.grid, wl.tile_hw), wl.block))
+    np.testing.assert_array_equal(res["order"], O.padded_order(order, wl.block))
     # scores: fp32 MFMA vs fp64
-    s64 = _oracle_scores(wl, inp)
+    s64 = _oracle_scores(wl, inp, order)
     err = np.abs(res["scores"].astype(np.float64) - s64).max()
     assert err <= S_REL * np.abs(s64).max(), f"score error {err}"
     # ranking, counts: bit-exact from the GPU's own fp32 scores
@@ -62,7 +62,7 @@ def check_routing_and_plan(wl, inp, res, p, refill):
     # placement: split tiles and the heaviest-first work list, for the
     # workgroup count the attention launch uses
     rows = H * nb
-    work, slot, nsplit = O.work_items(pl["kept"], F.attn_workgroups(problem_for(wl, p, refill)))
+    work, slot, nsplit = O.work_items(pl["kept"], F.attn_workgroups(problem_for(wl, p, refill, order=kind)))
     meta = res["plan_meta"]
     assert meta[0] == rows + nsplit and meta[1] == nsplit
     np.testing.assert_array_equal(meta[2: 2 + rows], slot)
@@ -72,9 +72,9 @@ def check_routing_and_plan(wl, inp, res, p, refill):
     return pl
 
 
-def check_attention(wl, inp, res, tiles=None, label=""):
+def check_attention(wl, inp, res, tiles=None, label="", order=None):
     q64, k64, v64 = f64_inputs(inp)
-    order = O.token_order(wl.grid, wl.tile_hw)
+    order = O.token_order(wl.grid, wl.tile_hw) if order is None else order
     scale = 1.0 / math.sqrt(wl.head_dim)
     o_ref, lse_ref = O.masked_attention(q64, k64, v64, order, wl.block, res["row_ptr"],
                                         res["col_idx"], scale, tiles)
@@ -293,3 +293,28 @@ def test_precise_block_importance_matches_oracle(name, refill):
     err = max(np.abs(got[h, i] - ref[h, i]).max() for h, i in rows)
     say(f"  importance max-abs {err:.2e} over {len(rows)} rows; split tiles {int(res['plan_meta'][1])}")
     assert err <= IMPORTANCE_ABS
+
+
+HILBERT = [
+    # name, heads, d, grid, block, p, k_min, refill, recipe
+    ("rank480p_hilbert", 5, 128, (21, 30, 52), 128, 0.95, 8, 0, "lograndom"),
+    ("odd_hilbert", 2, 128, (3, 13, 29), 64, 0.9, 2, 100, "lograndom"),
+    ("pow2_hilbert", 2, 64, (2, 32, 32), 128, 0.9, 2, 0, "tau1"),
+    ("strip_hilbert", 1, 128, (2, 5, 61), 64, 0.8, 1, 0, "conc_flat"),
+]
+
+
+@pytest.mark.parametrize("case", HILBERT, ids=[c[0] for c in HILBERT])
+def test_hilbert_order_chain(case):
+    """FVAttn S3.1 / GSRS A.6 Hilbert reordering: the GPU's index-to-cell
+    descent vs the oracle's enumeration, and the whole chain on that order."""
+    name, H, d, grid, block, p, kmin, refill, recipe = case
+    wl = Workload(name, H, d, grid, block, (p,), kmin, refill, seed=17, heads=recipe, tile=(0, 0))
+    say(f"[gpu] hilbert {name} N={wl.seq_len} nb={wl.num_blocks}")
+    inp = make_inputs(wl, cache=False)
+    q, k, v = device_inputs(inp)
+    order = O.hilbert_order(grid)
+    _, res = run_chain(problem_for(wl, p, refill, order="hilbert"), q, k, v)
+    check_routing_and_plan(wl, inp, res, p, refill, order=order, kind="hilbert")
+    tiles = None if H * res["nb"] <= 256 else sample_tiles(res["row_ptr"], H, res["nb"], per_head=8, seed=5)
+    check_attention(wl, inp, res, tiles, label=name, order=order)
