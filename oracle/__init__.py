@@ -7,3 +7,4 @@ product path never does.
 """
 
 from .fva_oracle import *  # noqa: F401,F403
+from . import fva_balance as balance  # noqa: F401

@@ -253,14 +253,22 @@ def kept_blocks(s_row: np.ndarray, count: int) -> np.ndarray:
 # Plan: one-GPU SASA refill, CSR mask, LPT tile order  ([FVA] S2.2, S3.2, S3.3)
 # --------------------------------------------------------------------------
 
-def refill_counts(row_count: np.ndarray, nb: int, refill_per_mille: int) -> np.ndarray:
+def refill_counts(row_count: np.ndarray, nb: int, refill_per_mille) -> np.ndarray:
+    """k'_i = k_i + min(nb - k_i, floor(k_i * f / 1000)); f is one value, or
+    one per row (a per-head refill repeated over the head's rows)."""
     rc = np.asarray(row_count, dtype=np.int64)
-    extra = np.minimum(nb - rc, (rc * int(refill_per_mille)) // 1000)
+    f = np.asarray(refill_per_mille, dtype=np.int64)
+    extra = np.minimum(nb - rc, (rc * f) // 1000)
     return rc + extra
 
 
-def plan(scores32: np.ndarray, row_count: np.ndarray, refill_per_mille: int) -> Dict[str, np.ndarray]:
+def plan(scores32: np.ndarray, row_count: np.ndarray, refill_per_mille: int,
+         head_refill: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """head_refill: optional refill per mille per head, replacing the single
+    value (the slack-driven budget of one-GPU SASA)."""
     H, nqb, nkb = scores32.shape
+    if head_refill is not None:
+        refill_per_mille = np.repeat(np.asarray(head_refill, dtype=np.int64), nqb)
     kept = refill_counts(row_count, nkb, refill_per_mille)
     row_ptr = np.zeros(H * nqb + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum(kept)
