@@ -5,18 +5,23 @@ include/fva.h); `adaptive_block_sparse_fva_amd.fva` is its ctypes binding.
 """
 
 from .fva import (  # noqa: F401
+    BalanceInfo,
+    BalanceParams,
     Buffers,
     FvaError,
     Problem,
     attn_workgroups,
+    balance,
+    balance_params,
     block_importance,
     load_library,
     make_problem,
     mfma_probe,
     plan,
     route,
+    sasa_refill,
     sizes,
     sparse_attn_fwd,
 )
 
-__version__ = "0.2.0"
+__version__ = "0.3.0"

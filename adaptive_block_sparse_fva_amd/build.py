@@ -41,20 +41,34 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libfva")
 
 
+# host-only C++ (no device code) is built by the host compiler
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def _host_cxx() -> str:
+    for cand in (shutil.which("g++"), shutil.which("c++")):
+        if cand:
+            return cand
+    raise RuntimeError("no host C++ compiler found")
 
 
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [_host_cxx(), *HOST_CFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc, *CFLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in line and "is not a recognized feature" not in line)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        raise RuntimeError(f"compile failed on {src}:\n{msg}")
     if verbose and msg.strip():
         print(msg, flush=True)
     return obj

@@ -14,7 +14,7 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
                  int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
                  float sm_scale, hipStream_t stream);
 int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked,
-                const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
+                const int32_t* row_count, const int32_t* head_refill, int32_t* row_ptr, int32_t* col_idx,
                 int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
                 uint32_t* tile_counter, hipStream_t stream);
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
@@ -148,7 +148,7 @@ using namespace fva;
 
 extern "C" {
 
-int fva_version(void) { return 200; }
+int fva_version(void) { return 300; }
 
 const char* fva_status_string(int status) {
   switch (status) {
@@ -216,7 +216,7 @@ int fva_route(const fva_problem* prob, const void* q, const void* k, const void*
 }
 
 int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_count,
-             int32_t* row_ptr, int32_t* col_idx, int32_t* head_count_final,
+             const int32_t* head_refill, int32_t* row_ptr, int32_t* col_idx, int32_t* head_count_final,
              int32_t* work_order, int32_t* plan_meta, uint32_t* tile_counter, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
@@ -228,8 +228,8 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_
   st = attn_grid(*prob, nb, &grid);
   if (st) return st;
   const int split_s = grid < FVA_MAX_SPLITS / 2 ? grid : FVA_MAX_SPLITS / 2;
-  return launch_plan(*prob, nb, split_s, ranked, row_count, row_ptr, col_idx, head_count_final,
-                     work_order, plan_meta, tile_counter, (hipStream_t)stream);
+  return launch_plan(*prob, nb, split_s, ranked, row_count, head_refill, row_ptr, col_idx,
+                     head_count_final, work_order, plan_meta, tile_counter, (hipStream_t)stream);
 }
 
 int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,

@@ -6,15 +6,23 @@
 // tiles are handed to compute units: longest first, so that the heavy heads do
 // not finish last.  S3.3: slack is turned into extra blocks taken, in the
 // routing's own ranking, after the ones already kept (no re-sort, no
-// re-scoring); here every row gets e_i = min(nb - k_i, k_i * refill / 1000).
+// re-scoring); here every row gets e_i = min(nb - k_i, k_i * f / 1000), with
+// f one value for the call or one per head (a budget turned into a refill).
 #include "fva_common.h"
 
 namespace fva {
 
 constexpr int PLAN_THREADS = 1024;
 
-__device__ __forceinline__ int refill_count(int k, int nb, int refill_per_mille) {
-  return k + min(nb - k, (k * refill_per_mille) / 1000);
+__device__ __forceinline__ int refill_count(int k, int nb, int f) {
+  return k + (int)min((int64_t)(nb - k), (int64_t)k * f / 1000);
+}
+
+// refill per mille of the head that row r belongs to
+__device__ __forceinline__ int row_refill(const int32_t* __restrict__ head_refill, int r, int nb,
+                                          int refill_per_mille) {
+  if (!head_refill) return refill_per_mille;
+  return min(max(head_refill[r / nb], 0), FVA_MAX_HEAD_REFILL);
 }
 
 // Sort key of a work item: length descending, then tile, then part.
@@ -33,7 +41,8 @@ __device__ __forceinline__ uint32_t item_key(int len, int tile, int part) {
 // larger than the mean.  Split tiles get slots 0, 1, ... in tile-id order.
 // Fewer than 2 * split_s tiles can qualify, and split_s <= FVA_MAX_SPLITS / 2.
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
-    const int32_t* __restrict__ row_count, int rows, int nb, int refill_per_mille, int split_s,
+    const int32_t* __restrict__ row_count, const int32_t* __restrict__ head_refill, int rows, int nb,
+    int refill_per_mille, int split_s,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_count_final,
     int32_t* __restrict__ work_order, int32_t* __restrict__ plan_meta,
     uint32_t* __restrict__ tile_counter) {
@@ -64,11 +73,15 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
     return base + incl - x;
   };
 
+  auto kept = [&](int r) {
+    return refill_count(row_count[r], nb, row_refill(head_refill, r, nb, refill_per_mille));
+  };
+
   // per-thread contiguous chunk of rows
   const int per = (rows + PLAN_THREADS - 1) / PLAN_THREADS;
   const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
   int local = 0;
-  for (int r = r0; r < r1; ++r) local += refill_count(row_count[r], nb, refill_per_mille);
+  for (int r = r0; r < r1; ++r) local += kept(r);
   int total = 0;
   int run = block_scan(local, &total);
 
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   // visible to the workgroup after the barrier inside the next scan)
   for (int r = r0; r < r1; ++r) {
     row_ptr[r] = run;
-    run += refill_count(row_count[r], nb, refill_per_mille);
+    run += kept(r);
   }
   if (r1 == rows && r0 < r1) row_ptr[rows] = run;
 
@@ -84,7 +97,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   const int mean = (total + split_s - 1) / split_s;
   auto is_split = [&](int kp) { return kp >= 2 && 2 * kp > mean; };
   int nsp = 0;
-  for (int r = r0; r < r1; ++r) nsp += is_split(refill_count(row_count[r], nb, refill_per_mille)) ? 1 : 0;
+  for (int r = r0; r < r1; ++r) nsp += is_split(kept(r)) ? 1 : 0;
   int nsplit = 0;
   int sp = block_scan(nsp, &nsplit);
   for (int hh = tid; hh < rows / nb; hh += PLAN_THREADS)
@@ -92,7 +105,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
 
   // work items: tile r's items start at r + (split tiles before r)
   for (int r = r0; r < r1; ++r) {
-    const int kp = refill_count(row_count[r], nb, refill_per_mille);
+    const int kp = kept(r);
     const int pos = r + sp;
     if (is_split(kp)) {
       plan_meta[2 + r] = sp;
@@ -192,11 +205,12 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
 }
 
 int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked,
-                const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
-                int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
-                uint32_t* tile_counter, hipStream_t stream) {
+                const int32_t* row_count, const int32_t* head_refill, int32_t* row_ptr,
+                int32_t* col_idx, int32_t* head_count_final, int32_t* work_order,
+                int32_t* plan_meta, uint32_t* tile_counter, hipStream_t stream) {
   const int rows = p.num_heads * nb;
-  plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, rows, nb, p.refill_per_mille, split_s,
+  plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, head_refill, rows, nb,
+                                                   p.refill_per_mille, split_s,
                                                    row_ptr, head_count_final, work_order, plan_meta,
                                                    tile_counter);
   int st = record_hip_error(hipGetLastError(), "plan_scan launch");

@@ -12,8 +12,9 @@ import ctypes
 import math
 import os
 from dataclasses import dataclass
-from typing import Optional, Sequence
+from typing import Dict, Optional, Sequence
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,16 @@ FVA_MAX_TILES = 16384
 FVA_MAX_SPLITS = 1024
 FVA_ORDER_TILES = 0
 FVA_ORDER_HILBERT = 1
+FVA_MAX_HEAD_REFILL = 1000 * (FVA_MAX_BLOCKS - 1)
+FVA_RLB_PAIRS = 0
+FVA_RLB_RING = 1
+FVA_BALANCE_NONE = 0
+FVA_BALANCE_SASA = 1
+FVA_BALANCE_RLB_SASA = 2
+FVA_RLB_MAX_PAIR_RANKS = 12
+FVA_RLB_MAX_RANKS = 64
+FVA_RLB_MAX_HEADS = 64
+FVA_RLB_MAX_HEAD_LOAD = 1 << 22
 
 EXPORTED = (
     "fva_sizes",
@@ -38,6 +49,8 @@ EXPORTED = (
     "fva_sparse_attn_fwd",
     "fva_block_importance",
     "fva_mfma_probe",
+    "fva_balance",
+    "fva_sasa_refill",
     "fva_status_string",
     "fva_last_error",
     "fva_version",
@@ -90,6 +103,32 @@ class Sizes(ctypes.Structure):
     ]
 
 
+class BalanceParams(ctypes.Structure):
+    _fields_ = [
+        ("num_ranks", ctypes.c_int32),
+        ("heads_per_rank", ctypes.c_int32),
+        ("topology", ctypes.c_int32),
+        ("k1_per_mille", ctypes.c_int32),
+        ("k2_per_mille", ctypes.c_int32),
+        ("n1_per_mille", ctypes.c_int32),
+        ("n2_per_mille", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class BalanceInfo(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("moves", ctypes.c_int32),
+        ("rho_per_mille", ctypes.c_int32),
+        ("rho_new_per_mille", ctypes.c_int32),
+        ("load_total", ctypes.c_int64),
+        ("load_max", ctypes.c_int64),
+        ("load_new_max", ctypes.c_int64),
+        ("load_aug_max", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -107,19 +146,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
     lib.fva_block_importance.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64,
                                    ctypes.POINTER(ctypes.c_double), vp]
+    BP = ctypes.POINTER(BalanceParams)
+    lib.fva_balance.argtypes = [BP, vp, vp, vp, vp, vp, vp, ctypes.POINTER(BalanceInfo)]
+    lib.fva_sasa_refill.argtypes = [BP, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
     lib.fva_last_error.argtypes = []
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
     for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
-                 "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_version"):
+                 "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_balance",
+                 "fva_sasa_refill", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,10 +232,12 @@ def route(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, works
 
 
 def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, work_order, plan_meta,
-         tile_counter, stream=None):
-    st = load_library().fva_plan(ctypes.byref(prob), _ptr(ranked), _ptr(row_count), _ptr(row_ptr),
-                                 _ptr(col_idx), _ptr(head_count_final), _ptr(work_order),
-                                 _ptr(plan_meta), _ptr(tile_counter), _stream(stream))
+         tile_counter, stream=None, head_refill=None):
+    """head_refill: optional device int32 [H], a refill per mille per head."""
+    st = load_library().fva_plan(ctypes.byref(prob), _ptr(ranked), _ptr(row_count),
+                                 _ptr(head_refill), _ptr(row_ptr), _ptr(col_idx),
+                                 _ptr(head_count_final), _ptr(work_order), _ptr(plan_meta),
+                                 _ptr(tile_counter), _stream(stream))
     _check(st, "fva_plan")
 
 
@@ -221,6 +266,61 @@ def mfma_probe(iters: int, random_operands: bool, sink: torch.Tensor, stream=Non
                                        sink.numel(), ctypes.byref(flops), _stream(stream))
     _check(st, "fva_mfma_probe")
     return float(flops.value)
+
+
+def balance_params(num_ranks: int, heads_per_rank: int, topology: str = "pairs",
+                   k1_per_mille: int = 1050, k2_per_mille: int = 1100, n1_per_mille: int = 800,
+                   n2_per_mille: int = 70) -> BalanceParams:
+    """Parameters of the cross-rank balance step; defaults are the paper's."""
+    kinds = {"pairs": FVA_RLB_PAIRS, "ring": FVA_RLB_RING}
+    if topology not in kinds:
+        raise FvaError(FVA_ERR_ARG, "balance_params", f"unknown topology {topology!r}")
+    return BalanceParams(num_ranks, heads_per_rank, kinds[topology], k1_per_mille, k2_per_mille,
+                         n1_per_mille, n2_per_mille, 0)
+
+
+def _host(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _hp(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def balance(prm: BalanceParams, head_load) -> Dict[str, object]:
+    """fva_balance on host arrays: head_load [R][Hl] -> the plan and budgets."""
+    R = prm.num_ranks
+    w = _host(head_load, np.int32)
+    if w.size != R * prm.heads_per_rank:
+        raise FvaError(FVA_ERR_ARG, "balance", "head_load must hold num_ranks * heads_per_rank values")
+    sigma = np.empty(R, np.int32)
+    send = np.empty(R, np.int32)
+    load_new = np.empty(R, np.int64)
+    slack = np.empty(R, np.int64)
+    budget = np.empty(R, np.int64)
+    info = BalanceInfo()
+    st = load_library().fva_balance(ctypes.byref(prm), _hp(w), _hp(sigma), _hp(send), _hp(load_new),
+                                    _hp(slack), _hp(budget), ctypes.byref(info))
+    _check(st, "fva_balance")
+    out = {name: getattr(info, name) for name, _ in BalanceInfo._fields_}
+    out.update(sigma=sigma, send=send, loads_new=load_new, slack=slack, budget=budget)
+    return out
+
+
+def sasa_refill(prm: BalanceParams, nb: int, row_count, send_head, budget):
+    """fva_sasa_refill on host arrays -> (head_refill int32 [R*Hl], added int64 [R])."""
+    R, Hl = prm.num_ranks, prm.heads_per_rank
+    rc = _host(row_count, np.int32)
+    send = _host(send_head, np.int32)
+    bud = _host(budget, np.int64)
+    if rc.size != R * Hl * nb or send.size != R or bud.size != R:
+        raise FvaError(FVA_ERR_ARG, "sasa_refill", "array sizes do not match the parameters")
+    refill = np.empty(R * Hl, np.int32)
+    added = np.empty(R, np.int64)
+    st = load_library().fva_sasa_refill(ctypes.byref(prm), int(nb), _hp(rc), _hp(send), _hp(bud),
+                                        _hp(refill), _hp(added))
+    _check(st, "fva_sasa_refill")
+    return refill, added
 
 
 @dataclass
@@ -278,9 +378,10 @@ class Buffers:
         route(self.prob, q, k, v, self.scores, self.ranked, self.row_count, self.head_count,
               self.order, self.kv, self.workspace, stream)
 
-    def plan(self, stream=None):
+    def plan(self, stream=None, head_refill=None):
         plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
-             self.head_count_final, self.work_order, self.plan_meta, self.tile_counter, stream)
+             self.head_count_final, self.work_order, self.plan_meta, self.tile_counter, stream,
+             head_refill)
 
     def attn(self, q, work_order=None, with_lse=True, block_lse=None, stream=None):
         """Attention over the K/V that the last route() call re-laid out, the

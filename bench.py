@@ -39,6 +39,8 @@ def parse():
                     help="wall-clock budget of the oracle's attention sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-dense", action="store_true")
+    ap.add_argument("--skip-balance", action="store_true",
+                    help="skip the eight-rank balance simulation (RLB + SASA)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device three times (a known byte count for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -139,6 +141,134 @@ def cpu_baseline(wl, inp, p, gpu_o, row_ptr_gpu, col_idx_gpu, budget_s):
         "sample_parity": {"o_max_abs": float(errs[:, 0].max()), "o_mean_abs": float(errs[:, 1].mean()),
                           "tiles": len(done)},
         "oracle_matches_gpu_mask": bool(np.array_equal(pl["row_ptr"], row_ptr_gpu)),
+    }
+
+
+def balance_simulation(stream, cpu_reps=200, reps=3):
+    """FVAttn S3.2-S3.3 on eight simulated ranks of five heads (the 480p-style
+    layer split across 8 GPUs), run one rank after another on this GPU.
+
+    The 40 heads are routed in one call; their kept-block counts go to the
+    host search (fva_balance: gating, one-head-per-rank migration plan, slack
+    budgets) and budget conversion (fva_sasa_refill).  Each rank's head set --
+    before migration, after it, and after it with the slack refill -- is then
+    gathered into its own buffers (one GPU's stand-in for the point-to-point
+    head transfer) and its plan + attention timed.  Reports the search time
+    and the imbalance of block counts and of measured attention times.
+    """
+    import numpy as np
+    import torch
+
+    import adaptive_block_sparse_fva_amd as F
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["world480p"]
+    R, Hl = 8, 5
+    H, N, d, B, p = wl.num_heads, wl.seq_len, wl.head_dim, wl.block, wl.top_p[0]
+    inp = make_inputs(wl, cache=False)
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    del inp
+    wprob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, p, wl.k_min, 0)
+    wbuf = F.Buffers.allocate(wprob)
+    wbuf.route(q, k, v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    wbuf.route(q, k, v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    world_route_ms = e0.elapsed_time(e1)
+    nb = wbuf.nb
+    hc = wbuf.head_count.cpu().numpy().astype(np.int64)
+    rc = wbuf.row_count.cpu().numpy().astype(np.int64)
+    del wbuf
+
+    def host_us(fn):
+        fn()
+        t0 = time.perf_counter()
+        for _ in range(cpu_reps):
+            fn()
+        return (time.perf_counter() - t0) / cpu_reps * 1e6
+
+    prm = F.balance_params(R, Hl, "pairs")
+    bal = F.balance(prm, hc.reshape(R, Hl))
+    refill, added = F.sasa_refill(prm, nb, rc, bal["send"], bal["budget"])
+    forced = F.balance_params(R, Hl, "pairs", 0, 0)
+    ring = F.balance_params(R, Hl, "ring", 0, 0)
+    timing_us = {
+        "balance_pairs": round(host_us(lambda: F.balance(forced, hc.reshape(R, Hl))), 1),
+        "balance_ring": round(host_us(lambda: F.balance(ring, hc.reshape(R, Hl))), 1),
+        "sasa_refill": round(host_us(lambda: F.sasa_refill(prm, nb, rc, bal["send"], bal["budget"])), 1),
+    }
+    ring_plan = F.balance(ring, hc.reshape(R, Hl))
+
+    sigma, send = bal["sigma"], bal["send"]
+    src = np.empty(R, np.int64)
+    src[sigma] = np.arange(R)
+
+    def heads_of(r, migrated):
+        own = [r * Hl + j for j in range(Hl)]
+        if not migrated or sigma[r] == r:
+            return own
+        s = int(src[r])
+        return [h for j, h in enumerate(own) if j != send[r]] + [s * Hl + int(send[s])]
+
+    rprob = F.make_problem(Hl, N, d, wl.grid, B, wl.tile_hw, p, wl.k_min, 0)
+    rbuf = F.Buffers.allocate(rprob)
+    schedules = {"routed": (False, False), "rlb": (True, False), "rlb_sasa": (True, True)}
+    attn_ms, plan_ms, kept = {}, {}, {}
+    for name, (migrated, sasa) in schedules.items():
+        attn_ms[name], plan_ms[name], kept[name] = [], [], []
+        for r in range(R):
+            idx = torch.tensor(heads_of(r, migrated), dtype=torch.long, device="cuda")
+            qr, kr, vr = (torch.index_select(x, 0, idx).contiguous() for x in (q, k, v))
+            f = refill[idx.cpu().numpy()] if sasa else np.zeros(Hl, np.int32)
+            fr = torch.from_numpy(np.ascontiguousarray(f, dtype=np.int32)).cuda()
+            rbuf.route(qr, kr, vr)
+            rbuf.plan(head_refill=fr)
+            rbuf.attn(qr)
+            torch.cuda.synchronize()
+            if not np.array_equal(rbuf.head_count.cpu().numpy(), hc[idx.cpu().numpy()]):
+                raise RuntimeError("a rank's routed counts differ from the world routing")
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            tp, ta = [], []
+            for _ in range(reps):
+                ev[0].record(stream)
+                rbuf.plan(head_refill=fr)
+                ev[1].record(stream)
+                rbuf.attn(qr)
+                ev[2].record(stream)
+                torch.cuda.synchronize()
+                tp.append(ev[0].elapsed_time(ev[1]))
+                ta.append(ev[1].elapsed_time(ev[2]))
+            plan_ms[name].append(round(float(np.median(tp)), 4))
+            attn_ms[name].append(round(float(np.median(ta)), 4))
+            kept[name].append(int(rbuf.row_ptr[-1].item()))
+    del rbuf
+
+    def rho(x):
+        x = np.asarray(x, dtype=np.float64)
+        return round(float(x.max() / x.mean()), 4)
+
+    return {
+        "world": "world480p: 8 ranks x 5 heads of the 480p-style layer, routed as one 40-head call",
+        "topology": "pairs", "k1_k2_n1_n2_per_mille": [1050, 1100, 800, 70],
+        "mode": int(bal["mode"]), "moves": int(bal["moves"]),
+        "sigma": sigma.tolist(), "send_head": send.tolist(),
+        "rank_blocks": {"routed": hc.reshape(R, Hl).sum(axis=1).tolist(),
+                        "rlb": bal["loads_new"].tolist(),
+                        "rlb_sasa": (bal["loads_new"] + added).tolist()},
+        "rho_blocks": {"routed": bal["rho_per_mille"] / 1000, "rlb": bal["rho_new_per_mille"] / 1000,
+                       "rlb_sasa": rho(bal["loads_new"] + added),
+                       "ring_rlb": ring_plan["rho_new_per_mille"] / 1000},
+        "budget": bal["budget"].tolist(), "blocks_added": added.tolist(),
+        "head_refill_per_mille": refill.tolist(),
+        "rank_attn_ms": attn_ms, "rank_plan_ms": plan_ms, "rank_kept_blocks": kept,
+        "rho_attn_time": {k2: rho(v2) for k2, v2 in attn_ms.items()},
+        "critical_attn_ms": {k2: max(v2) for k2, v2 in attn_ms.items()},
+        "host_us": timing_us,
+        "world_route_ms": round(world_route_ms, 4),
     }
 
 
@@ -317,6 +447,11 @@ def main():
         dense["order_comparison"] = order_cmp
         del hbuf
 
+    balance = None
+    if not args.skip_balance:
+        print("bench: eight-rank balance simulation", file=sys.stderr, flush=True)
+        balance = balance_simulation(stream)
+
     cpu = None
     if not args.skip_cpu_baseline:
         gpu_o = buf.o.float().cpu().numpy().astype(np.float64)
@@ -364,6 +499,7 @@ def main():
                          "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4)},
         "dense_reference": dense,
+        "balance": balance,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

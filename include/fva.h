@@ -68,6 +68,8 @@ enum fva_status {
 #define FVA_MAX_BLOCKS 2048
 #define FVA_MAX_TILES 16384
 #define FVA_MAX_SPLITS 1024
+/* Largest per-head refill per mille (fills every row that keeps >= 1 block). */
+#define FVA_MAX_HEAD_REFILL (1000 * (FVA_MAX_BLOCKS - 1))
 
 /*
  * The problem statement (FVAttn S2.1: per head h, query block i, key block j;
@@ -176,9 +178,14 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
  * Plan (FVAttn S3.2-S3.3 on one GPU: the placement step becomes a
  * heaviest-first work queue, slack augmentation a per-row refill).
  *   ranked, row_count   as written by fva_route, read only.
+ *   head_refill  device int32 [H] or NULL: refill per mille of each head,
+ *                replacing prob->refill_per_mille (for budgets from
+ *                fva_sasa_refill); values are clamped to
+ *                [0, FVA_MAX_HEAD_REFILL].
  *   row_ptr      device int32 [H*nb + 1], written: CSR row offsets of the
  *                final mask; row (h, i) keeps k'_i = k_i + e_i blocks with
- *                e_i = min(nb - k_i, floor(k_i * refill_per_mille / 1000)).
+ *                e_i = min(nb - k_i, floor(k_i * f_h / 1000)), f_h =
+ *                head_refill[h], or refill_per_mille without head_refill.
  *   col_idx      device int32 [>= row_ptr[H*nb]] (capacity H*nb*nb always
  *                suffices), written: the first k'_i ranked key blocks of each
  *                row, ascending.
@@ -200,7 +207,8 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
  * Queries the device for W (FVA_ERR_HIP without one).
  */
 int fva_plan(const fva_problem* prob, const int16_t* ranked,
-             const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
+             const int32_t* row_count, const int32_t* head_refill,
+             int32_t* row_ptr, int32_t* col_idx,
              int32_t* head_count_final, int32_t* work_order,
              int32_t* plan_meta, uint32_t* tile_counter, void* stream);
 
@@ -272,6 +280,108 @@ int fva_block_importance(const fva_problem* prob, const int32_t* order,
  */
 int fva_mfma_probe(int32_t iters, int32_t random_operands, float* sink,
                    int64_t sink_elems, double* flops, void* stream);
+
+/*
+ * Runtime load balancing and slack-aware augmentation across ranks
+ * (FVAttn S3.2 Eq 5-6, S3.3 Eq 7-10 and the rho gating; S4.1 defaults).
+ * Host only: these two calls make no HIP call and touch no device memory.
+ *
+ * R ranks each hold Hl heads, rank r the heads r*Hl .. r*Hl+Hl-1, with
+ * integer workloads (kept query-block x key-block tiles, head_count from
+ * fva_route).  Rank loads L_r are sums over the rank's heads and
+ * rho = max L / mean L (Eq 2).
+ *
+ * Gating: rho < k1 -> FVA_BALANCE_NONE; k1 <= rho < k2 -> FVA_BALANCE_SASA;
+ * rho >= k2 -> FVA_BALANCE_RLB_SASA, compared exactly as
+ * 1000 * R * max L >= k * sum L.  All-zero loads gate to NONE.
+ *
+ * RLB (only under FVA_BALANCE_RLB_SASA): a plan is a permutation sigma of the
+ * ranks; a rank with sigma(r) != r sends one of its heads, send_head[r], to
+ * sigma(r) and receives one from sigma^-1(r), so every rank moves at most one
+ * head out and one in (Eq 5: L_new_r = L_r - sent + received).  Candidates:
+ *   FVA_RLB_PAIRS  every involution (disjoint pairs of ranks, each pair swaps
+ *                  one head each way), R <= FVA_RLB_MAX_PAIR_RANKS;
+ *   FVA_RLB_RING   the identity and the cycle r -> r+1 mod R in which every
+ *                  rank sends one head, R <= FVA_RLB_MAX_RANKS.
+ * The chosen plan minimises, in order: max_r L_new_r; sum_r L_new_r^2 (the
+ * variance of Eq 6, since the total is fixed); the number of moved heads;
+ * sigma as a vector; send_head as a vector (-1 for ranks that send none).
+ * The result is a deterministic function of the inputs, so every rank can run
+ * the search on the same all-gathered loads and read off its own partners.
+ *
+ * SASA (under SASA and RLB_SASA): slack[r] = max L_new - L_new_r (Eq 7),
+ * budget[r] = floor(n1 * slack[r] / 1000) where 1000 * slack[r] >
+ * n2 * max L_new, else 0 (Eq 8 and the trigger); budget is 0 under NONE.
+ * With n1 <= 1000 no budget lifts a rank past max L_new (Eq 10's first term
+ * is 0).
+ */
+#define FVA_RLB_PAIRS 0
+#define FVA_RLB_RING 1
+#define FVA_BALANCE_NONE 0
+#define FVA_BALANCE_SASA 1
+#define FVA_BALANCE_RLB_SASA 2
+#define FVA_RLB_MAX_PAIR_RANKS 12
+#define FVA_RLB_MAX_RANKS 64
+#define FVA_RLB_MAX_HEADS 64
+#define FVA_RLB_MAX_HEAD_LOAD (1 << 22)  /* nb^2 at nb = 2048 */
+#define FVA_RLB_MAX_PER_MILLE 1000000
+
+typedef struct fva_balance_params {
+  int32_t num_ranks;       /* R >= 1 */
+  int32_t heads_per_rank;  /* Hl, 1 .. FVA_RLB_MAX_HEADS */
+  int32_t topology;        /* FVA_RLB_PAIRS or FVA_RLB_RING */
+  int32_t k1_per_mille;    /* SASA threshold on rho (1050) */
+  int32_t k2_per_mille;    /* RLB threshold on rho (1100), >= k1 */
+  int32_t n1_per_mille;    /* budget coefficient (800), 0 .. 1000 */
+  int32_t n2_per_mille;    /* trigger threshold on the slack (70) */
+  int32_t reserved;        /* must be 0 */
+} fva_balance_params;
+
+typedef struct fva_balance_info {
+  int32_t mode;              /* FVA_BALANCE_* chosen by the gating */
+  int32_t moves;             /* heads migrated (ranks with sigma(r) != r) */
+  int32_t rho_per_mille;     /* floor(1000 * rho) before, after RLB: */
+  int32_t rho_new_per_mille;
+  int64_t load_total;        /* sum L (unchanged by migration) */
+  int64_t load_max;          /* max L */
+  int64_t load_new_max;      /* max L_new: the critical path after RLB */
+  int64_t load_aug_max;      /* max (L_new + budget) (Eq 9) */
+} fva_balance_info;
+
+/*
+ *   prm          host, read during the call.
+ *   head_load    host int32 [R][Hl], each 0 .. FVA_RLB_MAX_HEAD_LOAD.
+ *   sigma, send_head   host int32 [R], written (send_head -1 = no move).
+ *   load_new, slack, budget   host int64 [R], written.
+ *   info         host, written.
+ * FVA_ERR_ARG for null pointers, loads out of range, reserved != 0, k1 > k2,
+ * n1 outside 0 .. 1000 or per-mille values outside 0 .. FVA_RLB_MAX_PER_MILLE;
+ * FVA_ERR_UNSUPPORTED for R or Hl past the limits above.
+ */
+int fva_balance(const fva_balance_params* prm, const int32_t* head_load,
+                int32_t* sigma, int32_t* send_head, int64_t* load_new,
+                int64_t* slack, int64_t* budget, fva_balance_info* info);
+
+/*
+ * One-GPU form of the augmentation (FVAttn S3.3: extra blocks follow the
+ * routing's ranking and skip the heads migrated out): turns each rank's block
+ * budget into one refill per mille f_r for the rank's heads that did not move
+ * (moved heads get 0).  With e_i = min(nb - k_i, floor(k_i f / 1000)) summed
+ * over the eligible rows as A(f), A* is the most blocks any f in
+ * [0, 1000 (nb - 1)] adds without exceeding budget[r], and f_r is the
+ * smallest f with A(f) = A*.
+ *   row_count    host int32 [R*Hl][nb] (fva_route's row_count per head),
+ *                each 0 .. nb.
+ *   send_head, budget   host, as written by fva_balance (budget >= 0).
+ *   head_refill  host int32 [R*Hl], written: f_r per head (fva_plan's
+ *                head_refill after a copy to the device).
+ *   added        host int64 [R], written: A* per rank.
+ * Errors as fva_balance, plus FVA_ERR_ARG for nb outside 1 .. FVA_MAX_BLOCKS.
+ */
+int fva_sasa_refill(const fva_balance_params* prm, int32_t nb,
+                    const int32_t* row_count, const int32_t* send_head,
+                    const int64_t* budget, int32_t* head_refill,
+                    int64_t* added);
 
 /* Static text for a status code. */
 const char* fva_status_string(int status);

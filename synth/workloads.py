@@ -92,6 +92,12 @@ WORKLOADS = {
         heads="lograndom",
         description="3 heads, d=128, 116160 tokens on 33x55x64, block 128, p sweep, k_min=8, "
                     "refill 100 per mille"),
+    # eight ranks' shares of the 480p-style layer (40 heads, rank r holds
+    # heads 5r .. 5r+4); head temperatures spread over all 40 heads
+    "world480p": Workload(
+        "world480p", 40, 128, (21, 30, 52), 128, (0.95,), 8, 0, seed=5, heads="lograndom",
+        description="8 ranks x 5 heads, d=128, 32760 tokens on 21x30x52, block 128, p=0.95, "
+                    "k_min=8; tau log-uniform in [0.3, 3] over the 40 heads"),
 }
 
 WORKLOAD_ORDER = ["tiny", "two_head", "rank480p", "rank720p", "long115k"]

@@ -110,7 +110,7 @@ def test_entry_points_reject_null_pointers_without_a_device():
     null = None
     st = lib.fva_route(ctypes.byref(p), *([null] * 10), 0, null)
     assert st == fva.FVA_ERR_ARG
-    st = lib.fva_plan(ctypes.byref(p), *([null] * 9))
+    st = lib.fva_plan(ctypes.byref(p), *([null] * 10))
     assert st == fva.FVA_ERR_ARG
     st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 12), 0, null)
     assert st == fva.FVA_ERR_ARG
