@@ -8,3 +8,4 @@ product path never does.
 
 from .fva_oracle import *  # noqa: F401,F403
 from . import fva_balance as balance  # noqa: F401
+from . import fva_gsrs as gsrs  # noqa: F401
