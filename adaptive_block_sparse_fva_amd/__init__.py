@@ -9,15 +9,19 @@ from .fva import (  # noqa: F401
     BalanceParams,
     Buffers,
     FvaError,
+    GsrsSchedule,
     Problem,
     attn_workgroups,
     balance,
     balance_params,
     block_importance,
+    gsrs_action,
+    gsrs_schedule,
     load_library,
     make_problem,
     mfma_probe,
     plan,
+    reselect,
     route,
     sasa_refill,
     sizes,

@@ -25,6 +25,9 @@ int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const voi
 int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* lse, const float* block_lse,
                             float* importance, hipStream_t stream);
+int launch_reselect(const fva_problem& p, int nb, const int32_t* row_ptr, const int32_t* col_idx,
+                    const float* importance, int16_t* ranked, int32_t* row_count,
+                    int32_t* head_count, hipStream_t stream);
 int attn_blocks_per_cu(int d, int block);
 
 static thread_local char g_last_error[256] = "";
@@ -265,6 +268,17 @@ int fva_block_importance(const fva_problem* prob, const int32_t* order, const in
   if (!order || !row_ptr || !col_idx || !lse || !block_lse || !importance) return FVA_ERR_ARG;
   return launch_block_importance(*prob, nb, order, row_ptr, col_idx, lse, block_lse, importance,
                                  (hipStream_t)stream);
+}
+
+int fva_reselect(const fva_problem* prob, const int32_t* row_ptr, const int32_t* col_idx,
+                 const float* importance, int16_t* ranked, int32_t* row_count,
+                 int32_t* head_count, void* stream) {
+  int nb = 0;
+  int st = check_problem(prob, &nb);
+  if (st) return st;
+  if (!row_ptr || !col_idx || !importance || !ranked || !row_count || !head_count) return FVA_ERR_ARG;
+  return launch_reselect(*prob, nb, row_ptr, col_idx, importance, ranked, row_count, head_count,
+                         (hipStream_t)stream);
 }
 
 }  // extern "C"

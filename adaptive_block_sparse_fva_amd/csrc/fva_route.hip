@@ -222,21 +222,10 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
 // ---------------------------------------------------------------------------
 constexpr int SEL_ROWS = 1;
 
-template <int E>  // keys per lane: the row padded to 64 E >= nb slots
-__device__ __forceinline__ int select_row(const float* __restrict__ scores, int nb, int row, float top_p,
-                                          int k_min, int16_t* __restrict__ ranked, int lane) {
-  constexpr int NP = 64 * E;
-  constexpr int LOG = __builtin_ctz(NP);
-  const float* s = scores + (int64_t)row * nb;
-
-  uint64_t key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int x = e * 64 + lane;
-    key[e] = x < nb ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x)) : 0ull;
-  }
-
-  // bitonic sort, descending over x = 64e + lane
+// Bitonic sort of the wave's 64 E keys, descending over slot x = 64e + lane.
+template <int E>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
+  constexpr int LOG = __builtin_ctz(64 * E);
   static_for<1, LOG + 1>([&](auto kl) {
     constexpr int KK = 1 << decltype(kl)::value;
     static_for<0, decltype(kl)::value>([&](auto jl) {
@@ -266,6 +255,52 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
       }
     });
   });
+}
+
+// Exact integer inclusive scan of the weights along the ranking; returns
+// #{slots with a weight-bearing entry whose prefix stays below ceil(p * W)},
+// W = the sum of all weights.  (Slots with zero weight past the ranked
+// entries are never below the target once the prefix has reached W.)
+template <int E>
+__device__ __forceinline__ int count_below_target(const uint64_t (&w)[E], const bool (&live)[E],
+                                                  float p, int lane) {
+  uint64_t prefix[E];
+  uint64_t carry = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint64_t incl = w[e];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t y = shfl_up_u64(incl, off);
+      if (lane >= off) incl += y;
+    }
+    prefix[e] = carry + incl;
+    const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)incl, 63, 64);
+    const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(incl >> 32), 63, 64);
+    carry += ((uint64_t)thi << 32) | tlo;
+  }
+  const double target = (double)p * (double)carry;
+  const uint64_t tint = (uint64_t)ceil(target);
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt += (live[e] && prefix[e] < tint) ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  return cnt;
+}
+
+template <int E>  // keys per lane: the row padded to 64 E >= nb slots
+__device__ __forceinline__ int select_row(const float* __restrict__ scores, int nb, int row, float top_p,
+                                          int k_min, int16_t* __restrict__ ranked, int lane) {
+  const float* s = scores + (int64_t)row * nb;
+
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = e * 64 + lane;
+    key[e] = x < nb ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x)) : 0ull;
+  }
+  sort_desc<E>(key, lane);
 
   int16_t* rk = ranked + (int64_t)row * nb;
 #pragma unroll
@@ -284,34 +319,86 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
     // weights along the ranking (pad slots weigh 0), exact integer scan
     const uint32_t top = (uint32_t)(__shfl((int)(uint32_t)(key[0] >> 32), 0, 64));
     const double smax = (double)from_orderable(top);
-    uint64_t prefix[E];
-    uint64_t carry = 0;
+    uint64_t w[E];
+    bool live[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int x = e * 64 + lane;
       const double sr = (double)from_orderable((uint32_t)(key[e] >> 32));
-      const uint64_t w = x < nb ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
-      uint64_t incl = w;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint64_t y = shfl_up_u64(incl, off);
-        if (lane >= off) incl += y;
-      }
-      prefix[e] = carry + incl;
-      const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)incl, 63, 64);
-      const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(incl >> 32), 63, 64);
-      carry += ((uint64_t)thi << 32) | tlo;
+      live[e] = x < nb;
+      w[e] = live[e] ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
     }
-    const double target = (double)p * (double)carry;
-    const uint64_t tint = (uint64_t)ceil(target);
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) cnt += (e * 64 + lane < nb && prefix[e] < tint) ? 1 : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-    kp = min(nb, cnt + 1);
+    kp = min(nb, count_below_target<E>(w, live, p, lane) + 1);
   }
   return max(kp, min(k_min, nb));
+}
+
+// Re-selection inside an evaluated set (growing sparsity with reduced
+// search): the row's evaluated blocks (its CSR entries) are ranked by their
+// precise importance, descending, equal values by lower id, and the other
+// blocks follow by ascending id; the weights are rint(importance * 2^40) of
+// the evaluated blocks, the cutoff the shortest prefix reaching p of their
+// sum, the floor min(k_min, evaluated count).  `bits` is this wave's LDS
+// membership bitmap (nb bits).
+template <int E>
+__device__ __forceinline__ int reselect_row(const float* __restrict__ importance, const int32_t* __restrict__ row_ptr,
+                                            const int32_t* __restrict__ col_idx, int nb, int row, float top_p,
+                                            int k_min, int16_t* __restrict__ ranked, uint32_t* bits, int lane) {
+  const int nwords = (nb + 31) >> 5;
+  if (lane < nwords) bits[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c0 = row_ptr[row], c = row_ptr[row + 1] - c0;
+  for (int j = lane; j < c; j += 64) {
+    const int b = col_idx[c0 + j];
+    atomicOr(&bits[b >> 5], 1u << (b & 31));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const float* v = importance + (int64_t)row * nb;
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = e * 64 + lane;
+    const uint64_t id = (uint64_t)(0xffffffffu - (uint32_t)x);
+    if (x >= nb)
+      key[e] = 0ull;
+    else if ((bits[x >> 5] >> (x & 31)) & 1u)
+      key[e] = ((uint64_t)orderable(v[x]) << 32) | id;  // >= 2^63 for importance >= 0
+    else
+      key[e] = id;
+  }
+  sort_desc<E>(key, lane);
+
+  int16_t* rk = ranked + (int64_t)row * nb;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = e * 64 + lane;
+    if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
+  }
+
+  int kp;
+  const float p = top_p;
+  if (p >= 1.0f) {
+    kp = c;
+  } else if (!(p > 0.0f)) {
+    kp = 0;
+  } else {
+    // the first c ranks are the evaluated blocks
+    uint64_t w[E];
+    bool live[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      live[e] = e * 64 + lane < c;
+      const double imp = fmax((double)from_orderable((uint32_t)(key[e] >> 32)), 0.0);
+      w[e] = live[e] ? (uint64_t)rint(imp * 1099511627776.0) : 0ull;  // 2^40
+    }
+    kp = min(c, count_below_target<E>(w, live, p, lane) + 1);
+  }
+  return max(kp, min(k_min, c));
 }
 
 template <int E>
@@ -346,6 +433,63 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0 && one_head) atomicAdd(&head_count[first / nb], wg_sum);
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void reselect_kernel(
+    const float* __restrict__ importance, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, int nb, int rows, float top_p, int k_min,
+    int16_t* __restrict__ ranked, int32_t* __restrict__ row_count, int32_t* __restrict__ head_count) {
+  __shared__ uint32_t bits[4][FVA_MAX_BLOCKS / 32];
+  __shared__ int wg_sum;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int first = blockIdx.x * 4;
+  const int last = min(rows, first + 4) - 1;
+  const bool one_head = first / nb == last / nb;
+  if (threadIdx.x == 0) wg_sum = 0;
+  __syncthreads();
+  const int row = first + wave;
+  if (row < rows) {  // uniform per wave
+    const int ki = reselect_row<E>(importance, row_ptr, col_idx, nb, row, top_p, k_min, ranked,
+                                   bits[wave], lane);
+    if (lane == 0) {
+      row_count[row] = ki;
+      if (one_head) atomicAdd(&wg_sum, ki);
+      else atomicAdd(&head_count[row / nb], ki);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && one_head) atomicAdd(&head_count[first / nb], wg_sum);
+}
+
+int launch_reselect(const fva_problem& p, int nb, const int32_t* row_ptr, const int32_t* col_idx,
+                    const float* importance, int16_t* ranked, int32_t* row_count,
+                    int32_t* head_count, hipStream_t stream) {
+  fill_i32_kernel<<<(p.num_heads + 255) / 256, 256, 0, stream>>>(head_count, p.num_heads, 0);
+  int st = record_hip_error(hipGetLastError(), "fill launch");
+  if (st) return st;
+  const int rows = p.num_heads * nb;
+  const int grid = (rows + 3) / 4;
+  int e = 1;
+  while (64 * e < nb) e <<= 1;
+#define FVA_RESELECT(E_)                                                                    \
+  reselect_kernel<E_><<<grid, 256, 0, stream>>>(importance, row_ptr, col_idx, nb, rows, p.top_p, \
+                                                p.k_min, ranked, row_count, head_count)
+  switch (e) {
+    case 1: FVA_RESELECT(1); break;
+    case 2: FVA_RESELECT(2); break;
+    case 4: FVA_RESELECT(4); break;
+    case 8: FVA_RESELECT(8); break;
+    case 16: FVA_RESELECT(16); break;
+    default: FVA_RESELECT(32); break;
+  }
+#undef FVA_RESELECT
+  return record_hip_error(hipGetLastError(), "reselect launch");
 }
 
 int launch_route(const fva_problem& p, int nb, const void* q, const void* k, const void* v,

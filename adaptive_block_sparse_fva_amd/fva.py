@@ -40,6 +40,11 @@ FVA_RLB_MAX_PAIR_RANKS = 12
 FVA_RLB_MAX_RANKS = 64
 FVA_RLB_MAX_HEADS = 64
 FVA_RLB_MAX_HEAD_LOAD = 1 << 22
+FVA_GSRS_MAX_SEARCHES = 16
+FVA_GSRS_DENSE = 0
+FVA_GSRS_FULL_SEARCH = 1
+FVA_GSRS_CANDIDATE_SEARCH = 2
+FVA_GSRS_REUSE = 3
 
 EXPORTED = (
     "fva_sizes",
@@ -51,6 +56,8 @@ EXPORTED = (
     "fva_mfma_probe",
     "fva_balance",
     "fva_sasa_refill",
+    "fva_reselect",
+    "fva_gsrs_action",
     "fva_status_string",
     "fva_last_error",
     "fva_version",
@@ -129,6 +136,17 @@ class BalanceInfo(ctypes.Structure):
     ]
 
 
+class GsrsSchedule(ctypes.Structure):
+    _fields_ = [
+        ("num_steps", ctypes.c_int32),
+        ("warmup_steps", ctypes.c_int32),
+        ("num_searches", ctypes.c_int32),
+        ("reduced", ctypes.c_int32),
+        ("search_step", ctypes.c_int32 * FVA_GSRS_MAX_SEARCHES),
+        ("top_p", ctypes.c_float * FVA_GSRS_MAX_SEARCHES),
+    ]
+
+
 _lib = None
 
 
@@ -155,6 +173,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     BP = ctypes.POINTER(BalanceParams)
     lib.fva_balance.argtypes = [BP, vp, vp, vp, vp, vp, vp, ctypes.POINTER(BalanceInfo)]
     lib.fva_sasa_refill.argtypes = [BP, ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.fva_reselect.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_gsrs_action.argtypes = [ctypes.POINTER(GsrsSchedule), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)]
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
     lib.fva_last_error.argtypes = []
@@ -162,7 +183,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_version.argtypes = []
     for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
                  "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_balance",
-                 "fva_sasa_refill", "fva_version"):
+                 "fva_sasa_refill", "fva_reselect", "fva_gsrs_action", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -321,6 +342,38 @@ def sasa_refill(prm: BalanceParams, nb: int, row_count, send_head, budget):
                                         _hp(refill), _hp(added))
     _check(st, "fva_sasa_refill")
     return refill, added
+
+
+def reselect(prob, row_ptr, col_idx, importance, ranked, row_count, head_count, stream=None):
+    """fva_reselect: re-selection with prob.top_p / prob.k_min inside the
+    evaluated mask (row_ptr, col_idx) from its precise importance."""
+    st = load_library().fva_reselect(ctypes.byref(prob), _ptr(row_ptr), _ptr(col_idx),
+                                     _ptr(importance), _ptr(ranked), _ptr(row_count),
+                                     _ptr(head_count), _stream(stream))
+    _check(st, "fva_reselect")
+
+
+def gsrs_schedule(num_steps: int, warmup_steps: int, search_steps: Sequence[int],
+                  top_ps: Sequence[float], reduced: bool = True) -> GsrsSchedule:
+    if len(search_steps) != len(top_ps) or len(search_steps) > FVA_GSRS_MAX_SEARCHES:
+        raise FvaError(FVA_ERR_ARG, "gsrs_schedule", "one p per search, at most 16 searches")
+    s = GsrsSchedule()
+    s.num_steps, s.warmup_steps = num_steps, warmup_steps
+    s.num_searches, s.reduced = len(search_steps), 1 if reduced else 0
+    for j, (t, p) in enumerate(zip(search_steps, top_ps)):
+        s.search_step[j] = int(t)
+        s.top_p[j] = float(p)
+    return s
+
+
+def gsrs_action(schedule: GsrsSchedule, step: int):
+    """fva_gsrs_action -> (action, p)."""
+    act = ctypes.c_int32(0)
+    p = ctypes.c_float(0.0)
+    st = load_library().fva_gsrs_action(ctypes.byref(schedule), int(step), ctypes.byref(act),
+                                        ctypes.byref(p))
+    _check(st, "fva_gsrs_action")
+    return int(act.value), float(p.value)
 
 
 @dataclass

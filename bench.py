@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-balance", action="store_true",
                     help="skip the eight-rank balance simulation (RLB + SASA)")
+    ap.add_argument("--skip-gsrs", action="store_true",
+                    help="skip the growing-sparsity / reduced-search trajectory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device three times (a known byte count for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -272,6 +274,85 @@ def balance_simulation(stream, cpu_reps=200, reps=3):
     }
 
 
+def gsrs_trajectory(stream, steps=10, warmup=2, at=(2, 4, 6, 8), ps=(0.95, 0.9, 0.85, 0.8)):
+    """GSRS S5.1 / A.5 / A.7 on a synthetic denoising trajectory of the
+    480p-style rank share (inputs of each step from synth.trajectory_step):
+    dense warm-up, searches with decreasing p, mask reuse between them; once
+    with reduced search (later searches over the first search's mask) and once
+    without (every search over all blocks).  Per step: time (HIP events around
+    the step's calls, route included), the evaluated density and the
+    attention recall against dense attention on the same inputs.  A search's
+    overhead is its step time minus the time of the reuse step after it."""
+    import numpy as np
+    import torch
+
+    import adaptive_block_sparse_fva_amd as F
+    from adaptive_block_sparse_fva_amd.gsrs import GsrsRunner
+    from synth import WORKLOADS
+    from synth.workloads import trajectory_parts, trajectory_step
+
+    wl = WORKLOADS["rank480p"]
+    H, N, d, B = wl.num_heads, wl.seq_len, wl.head_dim, wl.block
+    parts = trajectory_parts(wl, steps)
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    inputs = []
+    for t in range(steps):
+        x = trajectory_step(parts, t)
+        inputs.append((dev(x.q), dev(x.k), dev(x.v)))
+    del parts
+    prob = F.make_problem(H, N, d, wl.grid, B, wl.tile_hw, 1.0, wl.k_min, 0)
+    dense = F.Buffers.allocate(prob)
+    lse_dense = []
+    for q, k, v in inputs:
+        dense.run(q, k, v)
+        lse_dense.append(dense.lse.clone())
+    torch.cuda.synchronize()
+    del dense
+
+    out = {"workload": f"rank480p-shaped trajectory, {steps} steps (eta 0.5, kappa 0.5, beta 12)",
+           "warmup": warmup, "search_steps": list(at), "top_p": list(ps)}
+    for label, reduced in (("reduced_search", True), ("full_search", False)):
+        sched = F.gsrs_schedule(steps, warmup, list(at), list(ps), reduced)
+        for attempt in range(2):  # the first pass warms up, the second is timed
+            runner = GsrsRunner(prob, sched)
+            ms, acts, dens, rec = [], [], [], []
+            nb = runner.nb
+            for t, (q, k, v) in enumerate(inputs):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                act, _ = runner.step(t, q, k, v)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+                acts.append(act)
+                ev = int(runner.evaluated.row_ptr[-1].item())
+                dens.append(ev / (H * nb * nb))
+                rec.append(torch.exp(runner.buf.lse - lse_dense[t]).mean().item())
+        names = {F.fva.FVA_GSRS_DENSE: "dense", F.fva.FVA_GSRS_FULL_SEARCH: "full_search",
+                 F.fva.FVA_GSRS_CANDIDATE_SEARCH: "candidate_search", F.fva.FVA_GSRS_REUSE: "reuse"}
+        overhead, later = 0.0, 0.0
+        searches = [t for t, a in enumerate(acts)
+                    if a in (F.fva.FVA_GSRS_FULL_SEARCH, F.fva.FVA_GSRS_CANDIDATE_SEARCH)]
+        for t in searches:
+            if t + 1 < steps and acts[t + 1] == F.fva.FVA_GSRS_REUSE:
+                overhead += ms[t] - ms[t + 1]
+                if t != searches[0]:
+                    later += ms[t] - ms[t + 1]
+        out[label] = {"total_ms": round(sum(ms), 4), "step_ms": [round(x, 4) for x in ms],
+                      "actions": [names[a] for a in acts],
+                      "evaluated_density": [round(x, 4) for x in dens],
+                      "recall": [round(x, 4) for x in rec],
+                      "search_overhead_ms": round(overhead, 4),
+                      "later_search_overhead_ms": round(later, 4)}
+        del runner
+    r, f = out["reduced_search"]["search_overhead_ms"], out["full_search"]["search_overhead_ms"]
+    out["overhead_ratio_full_over_reduced"] = round(f / r, 3) if r > 0 else None
+    r2, f2 = (out["reduced_search"]["later_search_overhead_ms"],
+              out["full_search"]["later_search_overhead_ms"])
+    out["later_search_overhead_ratio"] = round(f2 / r2, 3) if r2 > 0 else None
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,6 +533,11 @@ def main():
         print("bench: eight-rank balance simulation", file=sys.stderr, flush=True)
         balance = balance_simulation(stream)
 
+    gsrs = None
+    if not args.skip_gsrs:
+        print("bench: growing-sparsity trajectory", file=sys.stderr, flush=True)
+        gsrs = gsrs_trajectory(stream)
+
     cpu = None
     if not args.skip_cpu_baseline:
         gpu_o = buf.o.float().cpu().numpy().astype(np.float64)
@@ -500,6 +586,7 @@ def main():
                          "natural": round(natural / ideal, 4)},
         "dense_reference": dense,
         "balance": balance,
+        "gsrs": gsrs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -266,6 +266,70 @@ int fva_block_importance(const fva_problem* prob, const int32_t* order,
                          float* importance, void* stream);
 
 /*
+ * Re-selection inside an evaluated set (GSRS S5.1 reduced search, S5.2 and
+ * A.4 Top-p, A.2 importance over the evaluated blocks): after an attention
+ * call over a mask with block_lse and fva_block_importance, choose each
+ * row's new kept blocks from among that mask's blocks.
+ *   row_ptr, col_idx  device, the evaluated mask (the one the importance was
+ *                computed over), read only; each row non-empty, ids < nb,
+ *                no repeats.
+ *   importance   device float [H][nb][nb] as written by fva_block_importance
+ *                for that mask, read only.
+ *   prob->top_p, prob->k_min   the search's threshold and floor (the rest of
+ *                prob as for the other calls).
+ *   ranked       device int16 [H][nb][nb], written: per row the evaluated
+ *                blocks by importance descending (equal values by lower id),
+ *                then the remaining blocks by ascending id.
+ *   row_count    device int32 [H*nb], written: k = max(k_p, min(k_min, c)),
+ *                c = the row's evaluated count, k_p = the shortest ranked
+ *                prefix whose weights rint(max(importance, 0) * 2^40) reach
+ *                fl(p * their sum) (1 if p reaches it with one block; c for
+ *                p >= 1; 0 for p <= 0).
+ *   head_count   device int32 [H], written: sum of row_count per head.
+ * fva_plan(ranked, row_count) then materialises the new mask, which is a
+ * subset of the evaluated one whenever refill is off.
+ */
+int fva_reselect(const fva_problem* prob, const int32_t* row_ptr,
+                 const int32_t* col_idx, const float* importance,
+                 int16_t* ranked, int32_t* row_count, int32_t* head_count,
+                 void* stream);
+
+/*
+ * Step schedule of growing sparsity with reduced search (GSRS S5.1, A.5;
+ * S6.1's default: 50 steps, 10 warm-up steps, searches at 10, 20, 30, 40
+ * with p = 0.95, 0.9, 0.85, 0.8).  Host only.
+ *   FVA_GSRS_DENSE             full attention (warm-up, or before any search)
+ *   FVA_GSRS_FULL_SEARCH       attention over every block with block LSEs,
+ *                              importance, re-selection with *top_p; at the
+ *                              first search past the warm-up (or every
+ *                              search when reduced = 0); its mask is the
+ *                              candidate set of the later searches
+ *   FVA_GSRS_CANDIDATE_SEARCH  the same over the candidate set only
+ *   FVA_GSRS_REUSE             attention over the latest selected mask
+ * A search step's output is its attention over the evaluated blocks.
+ * FVA_ERR_ARG for null pointers, step outside [0, num_steps), search steps
+ * not strictly increasing inside [0, num_steps), a NaN p, more than
+ * FVA_GSRS_MAX_SEARCHES searches or reduced not 0/1.
+ */
+#define FVA_GSRS_MAX_SEARCHES 16
+#define FVA_GSRS_DENSE 0
+#define FVA_GSRS_FULL_SEARCH 1
+#define FVA_GSRS_CANDIDATE_SEARCH 2
+#define FVA_GSRS_REUSE 3
+
+typedef struct fva_gsrs_schedule {
+  int32_t num_steps;      /* >= 1 */
+  int32_t warmup_steps;   /* >= 0 */
+  int32_t num_searches;   /* 0 .. FVA_GSRS_MAX_SEARCHES */
+  int32_t reduced;        /* 1: later searches over the candidate set only */
+  int32_t search_step[FVA_GSRS_MAX_SEARCHES];  /* strictly increasing */
+  float top_p[FVA_GSRS_MAX_SEARCHES];          /* p of each search */
+} fva_gsrs_schedule;
+
+int fva_gsrs_action(const fva_gsrs_schedule* schedule, int32_t step,
+                    int32_t* action, float* top_p);
+
+/*
  * Diagnostic (not part of the hot path): enqueue a kernel that runs only
  * bf16 MFMAs (v_mfma_f32_32x32x16_bf16, four independent chains per wave,
  * two 256-thread workgroups per compute unit) for `iters` rounds, with zero
