@@ -24,7 +24,7 @@ Readings where the pages leave a step open:
     (its block LSEs give the importance); the new mask serves the steps after;
   * re-selection ranks only the evaluated blocks (importance descending,
     equal importance by lower id) and the other blocks follow by ascending id;
-    the cutoff uses the weights w = rint(importance * 2^40) of the evaluated
+    the cutoff uses the weights w = rint(max(importance, 0) * 2^40) of the evaluated
     blocks, W their sum, k_p = min{k : sum_{r<k} w_(r) >= fl(p * W)}; p >= 1
     keeps every evaluated block, p <= 0 none before the floor; the Top-k
     floor is min(k_min, number of evaluated blocks);
@@ -66,7 +66,7 @@ def select_from_importance(imp32: np.ndarray, row_ptr: np.ndarray, col_idx: np.n
         elif not p > 0.0:
             kp = 0
         else:
-            w = [int(np.rint(float(vals[t]) * 2.0 ** FIXED_POINT_BITS)) for t in order]
+            w = [max(0, int(np.rint(float(vals[t]) * 2.0 ** FIXED_POINT_BITS))) for t in order]
             W = sum(w)
             target = p * float(W)          # one fp64 product, as fl(p * W)
             run, kp = 0, 0
