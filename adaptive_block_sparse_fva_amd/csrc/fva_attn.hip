@@ -79,6 +79,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, soff, 0, 0);
 }
 
+// Reductions over the two half-waves (lanes l and l ^ 32), in every lane,
+// without going through LDS: v_permlane32_swap of x with itself leaves x's
+// own and other-half values in the two results, in some order per lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_total(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Chunk swizzle of the LDS tiles: logical 16-byte chunk c of row r is stored
 // at position c ^ swz(r).  For 16 chunks per row (K, d = 128) swz swaps the
 // two 2-bit halves of r mod 16, a bijection on any 16 consecutive rows (the
@@ -116,15 +128,8 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int TILE = KB * D;   // elements of one K or V^T sub-tile
   static_assert(NW * 32 == BLK && SUB * KB == BLK && NI >= 1 && NI * RW == RPW, "tiling");
   static_assert(KB == 64 && NIV >= 1 && NIV * VRW == VRPW, "V^T tiling (64-key sub-blocks)");
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring slots");
-#ifndef FVA_S_AHEAD
-#define FVA_S_AHEAD 2
-#endif
-#ifndef FVA_V_AHEAD
-#define FVA_V_AHEAD 0
-#endif
-  constexpr int S_AHEAD = FVA_S_AHEAD;  // k-steps the K operand reads run ahead
-  constexpr int V_AHEAD = FVA_V_AHEAD;  // k-steps the V^T operand reads run ahead (0: compiler's choice)
+  static_assert(NBUF == 2, "two K and two V^T slots");
+  constexpr int DA = DS < 2 ? DS : 2;  // k-steps of S^T(u+1) issued with the row maximum
 
   // K sub-tiles: KB rows (keys) of D elements; V^T sub-tiles: D rows of KB
   // keys; 16-byte chunk c of row r stored at position c ^ swz(r).  The ring slots are separate LDS
@@ -250,70 +255,58 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
 
     // K and V^T sub-tiles of sub-block u: both start at byte pos * D * 2 of
     // their head's re-laid-out buffer
-    auto issue = [&](bf16_t* kt, bf16_t* vt, int u) {
+    auto issue_k = [&](bf16_t* kt, int u) {
       const int soff = __builtin_amdgcn_readfirstlane(sub_pos(u) * D * 2);
 #pragma unroll
       for (int m = 0; m < NI; ++m) lds_dma16(rk, kdma[m], soff, kt + (wave * RPW + m * RW) * D);
+    };
+    auto issue_v = [&](bf16_t* vt, int u) {
+      const int soff = __builtin_amdgcn_readfirstlane(sub_pos(u) * D * 2);
 #pragma unroll
       for (int m = 0; m < NIV; ++m) lds_dma16(rv, vdma[m], soff, vt + (wave * VRPW + m * VRW) * KB);
     };
-
-    // Prologue: sub-blocks 0 .. NBUF-2 in flight and landed.
-    issue(k_lds0, v_lds0, 0);
-    if constexpr (NBUF > 2) {
-      if (nsub > 1) issue(k_lds1, v_lds1, 1);
-    }
-    if constexpr (NBUF > 3) {
-      if (nsub > 2) issue(k_lds2, v_lds2, 2);
-    }
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // one sub-block: compute on slot CUR while later sub-blocks stream in
-    auto step = [&](auto cur_tag, int u) {
-      constexpr int CUR = decltype(cur_tag)::value;
-      constexpr int NXT = (CUR + NBUF - 1) % NBUF;
-      const bf16_t* ks = kslot(std::integral_constant<int, CUR>{});
-      const bf16_t* vs = vslot(std::integral_constant<int, CUR>{});
-      const int pos = sub_pos(u);
-      if (u + NBUF - 1 < nsub)
-        issue(kslot(std::integral_constant<int, NXT>{}), vslot(std::integral_constant<int, NXT>{}), u + NBUF - 1);
-
-      // ---- S^T = K Q^T for this wave's 32 queries ----
-      // The DS operand reads of a 32-key sub-tile are all issued before its
-      // MFMAs (the scheduling groups below keep them together), so LDS latency
-      // is paid once per sub-tile rather than once per MFMA.
-      f32x16 s[KS];
-      // matrix phases run at raised wave priority: the SIMD then issues this
-      // wave's MFMAs as soon as they are ready and fills the gaps with the
-      // other resident wave's softmax work
-      __builtin_amdgcn_s_setprio(1);
-      // The KS accumulation chains are interleaved (a dependent MFMA chain
-      // issues about a third slower than two independent ones), and the DS
-      // operand reads run two k-steps ahead of the MFMAs that use them.
+    // k-step d of S^T = K Q^T for the KS 32-key sub-tiles of one sub-block
+    // (the KS accumulation chains are independent, so their MFMAs interleave)
+    auto s_kstep = [&](f32x16(&sacc)[KS], const bf16_t* ks, int d) {
+      u32x4 kf[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kf[kk] = *reinterpret_cast<const u32x4*>(&ks[kk * 32 * D + koff[d]]);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
+        sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qf[d], sacc[kk],
+                                                           0, 0, 0);
+    };
+
+    // Software pipeline over the sub-blocks: the S^T MFMAs of sub-block u+1
+    // run while this wave's softmax of sub-block u is on the vector unit, so
+    // a wave keeps the matrix unit fed through its own vector work.  K runs
+    // one sub-block ahead of V: during step u the LDS ring holds K(u+1) and
+    // V(u) and receives K(u+2) and V(u+1).
+    issue_k(k_lds0, 0);
+    issue_v(v_lds0, 0);
+    if (nsub > 1) issue_k(k_lds1, 1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sa[KS], sb[KS];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int d = 0; d < DS; ++d) {
-        u32x4 kf[KS];
+      for (int r = 0; r < 16; ++r) sa[kk][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          kf[kk] = *reinterpret_cast<const u32x4*>(&ks[kk * 32 * D + koff[d]]);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]), qf[d], s[kk],
-                                                          0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, S_AHEAD * KS, 0);
-#pragma unroll
-      for (int d = 0; d < DS; ++d) {
-        __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
-        if (d + S_AHEAD < DS) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // s[kk][r] = q . k for key kk*32 + 8*(r/4) + 4*hf + r%4 of the sub-block
+    for (int d = 0; d < DS; ++d) s_kstep(sa, k_lds0, d);
+    __syncthreads();  // every wave has read K slot 0, which receives K(2)
+
+    // step u: sc holds S^T(u) (raw q.k); sn receives S^T(u+1).  At the last
+    // step the S^T of a sub-block past the end is computed from whatever the
+    // K slot holds and never used.
+    auto step = [&](auto cur_tag, f32x16(&sc)[KS], f32x16(&sn)[KS], int u) {
+      constexpr int CUR = decltype(cur_tag)::value;
+      constexpr int NXT = CUR ^ 1;
+      const bf16_t* kn = kslot(std::integral_constant<int, NXT>{});
+      const bf16_t* vs = vslot(std::integral_constant<int, CUR>{});
+      const int pos = sub_pos(u);
+      if (u + 2 < nsub) issue_k(kslot(std::integral_constant<int, CUR>{}), u + 2);
+      if (u + 1 < nsub) issue_v(vslot(std::integral_constant<int, NXT>{}), u + 1);
 
       // keys past the end of the sequence (only in the last block) get -inf
       // (a real branch: the empty asm keeps the compiler from turning it
@@ -325,20 +318,27 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (kk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) >= valid) s[kk][r] = -INFINITY;
+            if (kk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) >= valid) sc[kk][r] = -INFINITY;
       }
 
-      // ---- online softmax (base 2), row statistics per lane ----
-      // The running maximum m_run is only raised when a sub-block's maximum
-      // exceeds it by more than 8 (a factor 2^8), so most sub-blocks skip the
-      // rescale of the accumulators; weights then stay below 2^8, and the
-      // final division by the matching denominator makes the result exact.
+      // ---- phase A: the first k-steps of S^T(u+1) with the row maximum of
+      // S^T(u).  The running maximum m_run is only raised when a sub-block's
+      // maximum exceeds it by more than 8 (a factor 2^8), so most sub-blocks
+      // skip the rescale of the accumulators; weights then stay below 2^8,
+      // and the final division by the matching denominator makes the result
+      // exact.
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sn[kk][r] = 0.f;
+#pragma unroll
+      for (int d = 0; d < DA; ++d) s_kstep(sn, kn, d);
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
+      mx = halves_max(mx) * a.scale_log2;
       if (__any(mx > m_run + 8.0f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -350,44 +350,33 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
       }
+
+      // ---- phase B: the remaining k-steps of S^T(u+1), the weights of
+      // S^T(u) (base 2), and O^T += V^T P^T for sub-block u ----
+#pragma unroll
+      for (int d = DA; d < DS; ++d) s_kstep(sn, kn, d);
       float rs = 0.f;
+      bf16x8 pf[PS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
+      for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kk][r], a.scale_log2, -m_run));
-          s[kk][r] = p;
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[ps >> 1][(ps & 1) * 8 + e], a.scale_log2, -m_run));
           rs += p;
+          pf[ps][e] = (__bf16)p;
         }
       l_run += rs;
       blk_l += rs;
-
-      // ---- O^T += V^T P^T; the V^T operand of k-step ps and row tile d is
-      // one 16-byte LDS load ----
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
         u32x4 vf[DO];
 #pragma unroll
         for (int d = 0; d < DO; ++d) vf[d] = *reinterpret_cast<const u32x4*>(&vs[d * 32 * KB + voff[ps]]);
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[ps >> 1][(ps & 1) * 8 + e];
 #pragma unroll
         for (int d = 0; d < DO; ++d)
-          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[d]), pf, acc_o[d],
+          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[d]), pf[ps], acc_o[d],
                                                              0, 0, 0);
       }
-      if constexpr (V_AHEAD > 0) {
-        // V^T reads run V_AHEAD k-steps ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, V_AHEAD * DO, 0);
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-          __builtin_amdgcn_sched_group_barrier(0x008, DO, 0);
-          if (ps + V_AHEAD < PS) __builtin_amdgcn_sched_group_barrier(0x100, DO, 0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
 
       // GSRS S5.3 phase 1: after the last sub-block of a kept key block,
       // each query's log-sum-exp over that block's keys (natural log, same
@@ -395,35 +384,27 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       const bool rec = a.block_lse != nullptr && (u % SUB) == SUB - 1;
       float blk_lse = 0.f;
       if (rec) {
-        const float tot = blk_l + __shfl_xor(blk_l, 32, 64);
+        const float tot = halves_total(blk_l);
         blk_lse = (m_run + __log2f(tot)) * 0.69314718055994531f;
         blk_l = 0.f;
       }
 
-      // Sub-block u+1 has landed for every wave and every wave is done with
-      // slot CUR.  In steady state the loads issued in the last NBUF-2 steps
-      // may stay in flight; near the end wait for everything.
-      if (u + NBUF < nsub) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * (NI + NIV)));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // K(u+2) and V(u+1) have landed for every wave and every wave is done
+      // with K(u+1) and V(u)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
       // stored after the wait, so that the store completes behind the next
       // sub-block's work instead of stalling this one
       if (rec && hf == 0) a.block_lse[(int64_t)(c0 + u / SUB) * BLK + wave * 32 + l32] = blk_lse;
     };
-    for (int u = 0; u < nsub; u += NBUF) {
-      step(std::integral_constant<int, 0>{}, u);
-      if (u + 1 < nsub) step(std::integral_constant<int, 1>{}, u + 1);
-      if constexpr (NBUF > 2) {
-        if (u + 2 < nsub) step(std::integral_constant<int, 2 % NBUF>{}, u + 2);
-      }
-      if constexpr (NBUF > 3) {
-        if (u + 3 < nsub) step(std::integral_constant<int, 3 % NBUF>{}, u + 3);
-      }
+    for (int u = 0; u < nsub; u += 2) {
+      step(std::integral_constant<int, 0>{}, sa, sb, u);
+      if (u + 1 < nsub) step(std::integral_constant<int, 1>{}, sb, sa, u + 1);
     }
 
     // ---- normalise and store O (and LSE) for this lane's query, or leave
     // the part's partial result for the merge ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = halves_total(l_run);
     if (slot >= 0) {
       float* pp = a.partial + ((int64_t)slot * 2 + part) * (BLK * D + 2 * BLK);
       const int qrow = wave * 32 + l32;
