@@ -12,117 +12,144 @@
 namespace fva {
 
 // ---------------------------------------------------------------------------
-// 1. Pooling and re-layout.  One workgroup per (block b, head h, tensor
-// Q|K|V).  Q and K workgroups take the mean of the block's rows, accumulated
-// in fp32; the K workgroups also write the rows in position order (kp), and
-// the V workgroups write V transposed per 64-position sub-block (vt); the
-// layouts are those described with vt_key.  Memory bound: every byte of Q, K
-// and V is read exactly once with 16-byte loads, a row's 16-byte chunks
-// spread over consecutive lanes.  The Q workgroups of head 0 also publish the
-// order table, and workgroup (0,0,0) clears the per-head counters for the
-// select kernel.
+// 1. Pooling and re-layout.  One workgroup per (block b, head h): the mean
+// of the block's Q rows and of its K rows, accumulated in fp32, and the K
+// rows written in position order (kp).  V is
+// re-laid out (transposed per 64-position sub-block, vt) by extra workgroups
+// of the select launch, where its memory traffic overlaps the latency-bound
+// ranking; the layouts are those described with vt_key.  Memory bound: every
+// byte of Q, K and V is read exactly once with 16-byte loads, a row's 16-byte
+// chunks spread over consecutive lanes, all of a block's loads in flight
+// together.  The workgroups of head 0 also publish the order table, and
+// workgroup (0,0) clears the per-head counters for the select kernel.
 // ---------------------------------------------------------------------------
+
+// Where the V re-layout workgroups read and write.
+struct VRelayout {
+  const bf16_t* v;
+  int64_t stride_head, stride_token;
+  const int32_t* order;  // position -> token, -1 past the end (written by the pool kernel)
+  bf16_t* vt;
+  int block, nb, n;
+};
+
+// V of block b of head h, transposed per 64-position sub-block: a thread
+// gathers the 16-byte chunk dc (features 8dc .. 8dc+7) of the 8 keys that
+// make up output chunk jc (columns 8jc .. 8jc+7), transposes the 8 x 8 bf16
+// block in registers and writes 8 rows of 16 bytes.  The 8 keys of chunk jc
+// are vt_key(8jc + e) = 16(jc/2) + 4(jc%2) + 8(e/4) + e%4.  256 threads; tok
+// is 128 ints of LDS.
 template <int D>
-__global__ __launch_bounds__(256) void route_pool_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+__device__ __forceinline__ void vt_relayout_block(const VRelayout& r, int b, int h, int32_t* tok) {
+  const int tid = threadIdx.x;
+  const int block = r.block;
+  if (tid < block) tok[tid] = r.order[b * block + tid];
+  __syncthreads();
+  const int rb = min(block, r.n - b * block);
+  const int64_t npad = (int64_t)r.nb * block;
+  constexpr int DCH = D / 8;
+  constexpr int PER_SB = (VT_KEYS / 8) * DCH;
+  const bf16_t* x = r.v + (int64_t)h * r.stride_head;
+  for (int w = tid; w < (block / VT_KEYS) * PER_SB; w += 256) {
+    const int sb = w / PER_SB, rem = w % PER_SB;
+    const int jc = rem / DCH, dc = rem % DCH;
+    const int k0 = sb * VT_KEYS + 16 * (jc >> 1) + 4 * (jc & 1);
+    u32x4 in[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = k0 + 8 * (e >> 2) + (e & 3);
+      in[e] = u32x4{0u, 0u, 0u, 0u};
+      if (key < rb) in[e] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[key] * r.stride_token + dc * 8);
+    }
+    bf16_t* dst = r.vt + ((int64_t)h * npad + (int64_t)b * block + sb * VT_KEYS) * D + (8 * dc) * VT_KEYS + jc * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // feature 8dc + i of keys e = 0..7: the low (i even) or high (i odd)
+      // half of dword i/2 of each key's chunk, paired two keys per dword
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t o[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr)
+        o[pr] = __builtin_amdgcn_perm(in[2 * pr + 1][i >> 1], in[2 * pr][i >> 1], sel);
+      *reinterpret_cast<u32x4*>(dst + i * VT_KEYS) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
+// (at least 5 workgroups per compute unit, so that a 5-head problem's
+// workgroups are all resident at once)
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void route_pool_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     int64_t stride_head, int64_t stride_token, OrderGeo geo, int block,
     int nb, int num_heads, float* __restrict__ qbar, float* __restrict__ kbar,
     int32_t* __restrict__ order, int32_t* __restrict__ head_count,
-    bf16_t* __restrict__ kp, bf16_t* __restrict__ vt) {
+    bf16_t* __restrict__ kp) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RG = 256 / CH;   // rows in flight per pass
   constexpr int MAXIT = 128 / RG;
   __shared__ int32_t tok[128];
-  __shared__ float part[RG][D];
+  __shared__ float part[2][RG][D];
 
-  const int b = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
+  const int b = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int rb = min(block, geo.n - b * block);
   if (tid < block) {
     const int t = geo.token(b * block + tid);
     tok[tid] = t;
-    if (which == 0 && h == 0) order[b * block + tid] = t;
+    if (h == 0) order[b * block + tid] = t;
   }
-  if (b == 0 && h == 0 && which == 0)
+  if (b == 0 && h == 0)
     for (int i = tid; i < num_heads; i += 256) head_count[i] = 0;
   __syncthreads();
 
   const int64_t npad = (int64_t)nb * block;
   const int c = tid % CH, rg = tid / CH;
-  if (which == 2) {
-    // V, transposed per 64-position sub-block: a thread gathers the 16-byte
-    // chunk dc (features 8dc .. 8dc+7) of the 8 keys that make up output
-    // chunk jc (columns 8jc .. 8jc+7), transposes the 8 x 8 bf16 block in
-    // registers and writes 8 rows of 16 bytes.  The 8 keys of chunk jc are
-    // vt_key(8jc + e) = 16(jc/2) + 4(jc%2) + 8(e/4) + e%4.
-    constexpr int DCH = D / 8;
-    constexpr int PER_SB = (VT_KEYS / 8) * DCH;
-    const bf16_t* x = v + (int64_t)h * stride_head;
-    for (int w = tid; w < (block / VT_KEYS) * PER_SB; w += 256) {
-      const int sb = w / PER_SB, rem = w % PER_SB;
-      const int jc = rem / DCH, dc = rem % DCH;
-      const int k0 = sb * VT_KEYS + 16 * (jc >> 1) + 4 * (jc & 1);
-      u32x4 in[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = k0 + 8 * (e >> 2) + (e & 3);
-        in[e] = u32x4{0u, 0u, 0u, 0u};
-        if (key < rb) in[e] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[key] * stride_token + dc * 8);
-      }
-      bf16_t* dst = vt + ((int64_t)h * npad + (int64_t)b * block + sb * VT_KEYS) * D + (8 * dc) * VT_KEYS + jc * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // feature 8dc + i of keys e = 0..7: the low (i even) or high (i odd)
-        // half of dword i/2 of each key's chunk, paired two keys per dword
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t o[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr)
-          o[pr] = __builtin_amdgcn_perm(in[2 * pr + 1][i >> 1], in[2 * pr][i >> 1], sel);
-        *reinterpret_cast<u32x4*>(dst + i * VT_KEYS) = u32x4{o[0], o[1], o[2], o[3]};
-      }
-    }
-    return;
-  }
 
-  const bf16_t* x = (which == 0 ? q : k) + (int64_t)h * stride_head;
-  u32x4 rows[MAXIT];
+  // every row of the block's Q and K in flight at once
+  const bf16_t* xq = q + (int64_t)h * stride_head;
+  const bf16_t* xk = k + (int64_t)h * stride_head;
+  u32x4 qrows[MAXIT], krows[MAXIT];
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
     const int r = rg + it * RG;
-    if (r < rb)
-      rows[it] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[r] * stride_token + c * 8);
-    else
-      rows[it] = u32x4{0u, 0u, 0u, 0u};
-  }
-  if (which == 1) {
-    // K rows in position order, zero rows past the end
-    bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
-#pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-      const int r = rg + it * RG;
-      if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = rows[it];
+    qrows[it] = krows[it] = u32x4{0u, 0u, 0u, 0u};
+    if (r < rb) {
+      const int64_t off = (int64_t)tok[r] * stride_token + c * 8;
+      qrows[it] = *reinterpret_cast<const u32x4*>(xq + off);
+      krows[it] = *reinterpret_cast<const u32x4*>(xk + off);
     }
   }
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  // K rows in position order, zero rows past the end
+  bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
-    acc[0] += bf16_lo(rows[it].x); acc[1] += bf16_hi(rows[it].x);
-    acc[2] += bf16_lo(rows[it].y); acc[3] += bf16_hi(rows[it].y);
-    acc[4] += bf16_lo(rows[it].z); acc[5] += bf16_hi(rows[it].z);
-    acc[6] += bf16_lo(rows[it].w); acc[7] += bf16_hi(rows[it].w);
+    const int r = rg + it * RG;
+    if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = krows[it];
   }
+  auto column_sums = [&](const u32x4(&rows)[MAXIT], float(&pt)[RG][D]) {
+    float acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][c * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      acc[0] += bf16_lo(rows[it].x); acc[1] += bf16_hi(rows[it].x);
+      acc[2] += bf16_lo(rows[it].y); acc[3] += bf16_hi(rows[it].y);
+      acc[4] += bf16_lo(rows[it].z); acc[5] += bf16_hi(rows[it].z);
+      acc[6] += bf16_lo(rows[it].w); acc[7] += bf16_hi(rows[it].w);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pt[rg][c * 8 + e] = acc[e];
+  };
+  column_sums(qrows, part[0]);
+  column_sums(krows, part[1]);
   __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
+  if (tid < 2 * D) {
+    const int which = tid / D, col = tid % D;
+    float sum = 0.f;
 #pragma unroll 8
-    for (int g = 0; g < RG; ++g) s += part[g][tid];
+    for (int g = 0; g < RG; ++g) sum += part[which][g][col];
     float* out = (which == 0 ? qbar : kbar) + ((int64_t)h * nb + b) * D;
-    out[tid] = s / (float)rb;
+    out[col] = sum / (float)rb;
   }
 }
 
@@ -192,10 +219,38 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+// Value of lane l ^ M (M a power of two below 64) without going through
+// LDS: DPP quad permutations for 1 and 2; for 4 the half-row mirror (l ^ 7)
+// then l ^ 3, for 8 the row mirror (l ^ 15) then the half-row mirror; for 16
+// and 32 the permlane swaps of x with itself, whose two results hold this
+// lane's and its partner's values in some order (so their sum minus x, in
+// wrapping integer arithmetic, is the partner's).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  const int v = (int)x;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);
+  } else if constexpr (M == 4) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false), 0x1B, 0xf, 0xf,
+                                              false);
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, false), 0x141, 0xf,
+                                              0xf, false);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return r[0] + r[1] - x;
+  } else {
+    static_assert(M == 32, "lane xor below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return r[0] + r[1] - x;
+  }
+}
+
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
+  return ((uint64_t)xor_lane<M>((uint32_t)(x >> 32)) << 32) | xor_lane<M>((uint32_t)x);
 }
 
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
@@ -248,7 +303,7 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const bool desc = ((e * 64 + lane) & KK) == 0;
-          const uint64_t a = key[e], b = shfl_xor_u64(a, JJ);
+          const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
           const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
           key[e] = (lower == desc) ? hi : lo;
         }
@@ -275,8 +330,8 @@ __device__ __forceinline__ int count_below_target(const uint64_t (&w)[E], const 
       if (lane >= off) incl += y;
     }
     prefix[e] = carry + incl;
-    const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)incl, 63, 64);
-    const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(incl >> 32), 63, 64);
+    const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+    const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63);
     carry += ((uint64_t)thi << 32) | tlo;
   }
   const double target = (double)p * (double)carry;
@@ -317,7 +372,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
     kp = 0;
   } else {
     // weights along the ranking (pad slots weigh 0), exact integer scan
-    const uint32_t top = (uint32_t)(__shfl((int)(uint32_t)(key[0] >> 32), 0, 64));
+    const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[0] >> 32), 0);
     const double smax = (double)from_orderable(top);
     uint64_t w[E];
     bool live[E];
@@ -401,11 +456,20 @@ __device__ __forceinline__ int reselect_row(const float* __restrict__ importance
   return max(kp, min(k_min, c));
 }
 
-template <int E>
+// The launch also carries the V re-layout: workgroups sel_wgs .. sel_wgs +
+// H*nb - 1 each transpose one (head, block) of V (vt_relayout_block), so that
+// the memory traffic overlaps the latency-bound ranking.
+template <int E, int D>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const float* __restrict__ scores, int nb, int rows, float top_p, int k_min,
     int16_t* __restrict__ ranked, int32_t* __restrict__ row_count,
-    int32_t* __restrict__ head_count) {
+    int32_t* __restrict__ head_count, int sel_wgs, VRelayout vr) {
+  if ((int)blockIdx.x >= sel_wgs) {
+    __shared__ int32_t tok[128];
+    const int w = blockIdx.x - sel_wgs;
+    vt_relayout_block<D>(vr, w % vr.nb, w / vr.nb, tok);
+    return;
+  }
   __shared__ int wg_sum;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int first = blockIdx.x * 4 * SEL_ROWS;
@@ -497,17 +561,17 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
                  int32_t* head_count, int32_t* order, void* kv, float* qbar, float* kbar,
                  float sm_scale, hipStream_t stream) {
   const OrderGeo geo = make_order_geo(p);
-  const dim3 pool_grid(nb, p.num_heads, 3);
+  const dim3 pool_grid(nb, p.num_heads);
   bf16_t* kp = (bf16_t*)kv;
   bf16_t* vt = kp + (int64_t)p.num_heads * nb * p.block * p.head_dim;
   if (p.head_dim == 128)
     route_pool_kernel<128><<<pool_grid, 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, p.stride_head, p.stride_token, geo,
-        p.block, nb, p.num_heads, qbar, kbar, order, head_count, kp, vt);
+        (const bf16_t*)q, (const bf16_t*)k, p.stride_head, p.stride_token, geo, p.block, nb,
+        p.num_heads, qbar, kbar, order, head_count, kp);
   else
     route_pool_kernel<64><<<pool_grid, 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, p.stride_head, p.stride_token, geo,
-        p.block, nb, p.num_heads, qbar, kbar, order, head_count, kp, vt);
+        (const bf16_t*)q, (const bf16_t*)k, p.stride_head, p.stride_token, geo, p.block, nb,
+        p.num_heads, qbar, kbar, order, head_count, kp);
   int st = record_hip_error(hipGetLastError(), "route_pool launch");
   if (st) return st;
 
@@ -519,18 +583,33 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   st = record_hip_error(hipGetLastError(), "route_scores launch");
   if (st) return st;
 
+  // the select launch also carries the V re-layout, one workgroup per
+  // (head, block); a share of it in the scores launch was slower (those
+  // workgroups would hold the score tiles' 66 KB of LDS each)
   const int rows = p.num_heads * nb;
-  const int sel_grid = (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
+  const VRelayout vr{(const bf16_t*)v, p.stride_head, p.stride_token, order, vt, p.block, nb, p.seq_len};
+  const int sel_wgs = (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
+  const int grid = sel_wgs + rows;
   int e = 1;
   while (64 * e < nb) e <<= 1;
+#define FVA_SELECT(E_)                                                                               \
+  do {                                                                                               \
+    if (p.head_dim == 128)                                                                           \
+      route_select_kernel<E_, 128><<<grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, \
+                                                             row_count, head_count, sel_wgs, vr);    \
+    else                                                                                             \
+      route_select_kernel<E_, 64><<<grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked,  \
+                                                            row_count, head_count, sel_wgs, vr);    \
+  } while (0)
   switch (e) {
-    case 1: route_select_kernel<1><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
-    case 2: route_select_kernel<2><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
-    case 4: route_select_kernel<4><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
-    case 8: route_select_kernel<8><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
-    case 16: route_select_kernel<16><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
-    default: route_select_kernel<32><<<sel_grid, 256, 0, stream>>>(scores, nb, rows, p.top_p, p.k_min, ranked, row_count, head_count); break;
+    case 1: FVA_SELECT(1); break;
+    case 2: FVA_SELECT(2); break;
+    case 4: FVA_SELECT(4); break;
+    case 8: FVA_SELECT(8); break;
+    case 16: FVA_SELECT(16); break;
+    default: FVA_SELECT(32); break;
   }
+#undef FVA_SELECT
   return record_hip_error(hipGetLastError(), "route_select launch");
 }
 
