@@ -155,23 +155,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
 
 // ---------------------------------------------------------------------------
 // 2. Block scores S_h = sm_scale * Qbar_h Kbar_h^T with fp32 MFMA
-// (v_mfma_f32_32x32x2f32).  A workgroup owns a 64 x 64 tile of S; each of its
-// four waves a 32 x 32 quarter.  Operands are staged in LDS with one float of
-// row padding so that the 32 rows a wave reads at one column hit 32 banks.
+// (v_mfma_f32_32x32x2f32).  A workgroup owns a 32 x 32 tile of S and its
+// four waves split the contraction over d into quarters, so that the short
+// dependent MFMA chains of many tiles run on all compute units at once; the
+// partial tiles are added in LDS in wave order.  Operands are staged in LDS
+// with one float of row padding so that the 32 rows a wave reads at one
+// column hit 32 banks.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void route_scores_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int nb,
     float sm_scale, float* __restrict__ scores) {
   constexpr int LD = D + 1;
-  __shared__ float qs[64 * LD];
-  __shared__ float ks[64 * LD];
+  constexpr int KQ = D / 4;  // contraction slice of one wave
+  __shared__ float qs[32 * LD];
+  __shared__ float ks[32 * LD];
+  __shared__ float part[4][32 * 33];
   const int h = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   const int tid = threadIdx.x;
   const float* qh = qbar + (int64_t)h * nb * D;
   const float* kh = kbar + (int64_t)h * nb * D;
-  for (int idx = tid; idx < 64 * D / 4; idx += 256) {
+  for (int idx = tid; idx < 32 * D / 4; idx += 256) {
     const int r = idx / (D / 4), c4 = idx % (D / 4);
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
     if (i0 + r < nb) a = *reinterpret_cast<const f32x4*>(qh + (int64_t)(i0 + r) * D + c4 * 4);
@@ -184,25 +189,25 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
   const int l32 = lane & 31, hf = lane >> 5;
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const float* qrow = qs + (wm * 32 + l32) * LD + hf;
-  const float* krow = ks + (wn * 32 + l32) * LD + hf;
-#pragma unroll 8
-  for (int kk = 0; kk < D; kk += 2)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qrow[kk], krow[kk], acc, 0, 0, 0);
-  // acc[r] holds S[i0 + wm*32 + 8*(r/4) + 4*hf + r%4][j0 + wn*32 + l32]
-  const int j = j0 + wn * 32 + l32;
-  if (j < nb) {
-    float* out = scores + (int64_t)h * nb * nb + j;
+  const float* qrow = qs + l32 * LD + hf + wave * KQ;
+  const float* krow = ks + l32 * LD + hf + wave * KQ;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + wm * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (i < nb) out[(int64_t)i * nb] = sm_scale * acc[r];
-    }
+  for (int kk = 0; kk < KQ; kk += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qrow[kk], krow[kk], acc, 0, 0, 0);
+  // acc[r] holds this wave's part of S[i0 + 8*(r/4) + 4*hf + r%4][j0 + l32]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[wave][(8 * (r >> 2) + 4 * hf + (r & 3)) * 33 + l32] = acc[r];
+  __syncthreads();
+  for (int x = tid; x < 32 * 32; x += 256) {
+    const int ii = x >> 5, jj = x & 31;
+    const int i = i0 + ii, j = j0 + jj;
+    const int o = ii * 33 + jj;
+    const float sum = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];
+    if (i < nb && j < nb) scores[(int64_t)h * nb * nb + (int64_t)i * nb + j] = sm_scale * sum;
   }
 }
 
@@ -575,7 +580,7 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   int st = record_hip_error(hipGetLastError(), "route_pool launch");
   if (st) return st;
 
-  const dim3 sc_grid((nb + 63) / 64, (nb + 63) / 64, p.num_heads);
+  const dim3 sc_grid((nb + 31) / 32, (nb + 31) / 32, p.num_heads);
   if (p.head_dim == 128)
     route_scores_kernel<128><<<sc_grid, 256, 0, stream>>>(qbar, kbar, nb, sm_scale, scores);
   else
