@@ -9,6 +9,7 @@
 // re-scoring); here every row gets e_i = min(nb - k_i, k_i * f / 1000), with
 // f one value for the call or one per head (a budget turned into a refill).
 #include "fva_common.h"
+#include "fva_lanes.h"
 
 namespace fva {
 
@@ -28,6 +29,65 @@ __device__ __forceinline__ int row_refill(const int32_t* __restrict__ head_refil
 // Sort key of a work item: length descending, then tile, then part.
 __device__ __forceinline__ uint32_t item_key(int len, int tile, int part) {
   return ((uint32_t)(FVA_MAX_BLOCKS - len) << 15) | ((uint32_t)tile << 1) | (uint32_t)part;
+}
+
+// NS consecutive stages of bitonic merge level kk, compare distances jj,
+// jj/2, .., jj >> (NS-1), done as one round: the 2^NS elements whose indices
+// differ only in those NS bits form a group that the stages never leave, and
+// they share the level's direction bit (kk lies above jj), so a thread loads
+// a group into registers, applies the NS stages in order and writes it back.
+// Same compare-exchanges as the stage-by-stage network, one LDS round trip
+// and one barrier per round.
+template <int NS>
+__device__ __forceinline__ void sort_round(uint32_t* keys, int ipad, int kk, int jj, int tid) {
+  constexpr int G = 1 << NS;
+  const int low = jj >> (NS - 1);
+  for (int g = tid; g < (ipad >> NS); g += PLAN_THREADS) {
+    const int base = ((g & ~(low - 1)) << NS) | (g & (low - 1));
+    const bool asc = (base & kk) == 0;
+    uint32_t v[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) v[m] = keys[base + m * low];
+#pragma unroll
+    for (int st = NS - 1; st >= 0; --st)
+#pragma unroll
+      for (int m = 0; m < G; ++m)
+        if (!(m & (1 << st))) {
+          const uint32_t a = v[m], b = v[m | (1 << st)];
+          const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
+          v[m] = asc ? lo : hi;
+          v[m | (1 << st)] = asc ? hi : lo;
+        }
+#pragma unroll
+    for (int m = 0; m < G; ++m) keys[base + m * low] = v[m];
+  }
+  __syncthreads();
+}
+
+// Stages J0, J0/2, .., 1 of bitonic merge level kk on one wave's chunk of
+// 128 keys at offset base, held two per lane (chunk slot 64e + lane in
+// v[e]): distance 64 pairs a lane's two keys, smaller distances pair lanes
+// (DPP / permlane exchanges).  Every such stage stays inside the chunk.
+template <int J0>
+__device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int base, int kk) {
+  static_for<0, __builtin_ctz(J0) + 1>([&](auto sl) {
+    constexpr int JJ = J0 >> decltype(sl)::value;
+    if constexpr (JJ == 64) {
+      const bool asc = ((base + lane) & kk) == 0;
+      const uint32_t lo = v[0] < v[1] ? v[0] : v[1], hi = v[0] < v[1] ? v[1] : v[0];
+      v[0] = asc ? lo : hi;
+      v[1] = asc ? hi : lo;
+    } else {
+      const bool lower = (lane & JJ) == 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool asc = ((base + 64 * e + lane) & kk) == 0;
+        const uint32_t a = v[e], b = xor_lane<JJ>(a);
+        const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
+        v[e] = (lower == asc) ? lo : hi;
+      }
+    }
+  });
 }
 
 // One workgroup: final counts, CSR row offsets, per-head totals, the split
@@ -119,35 +179,37 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
     }
   }
   const int nitems = rows + nsplit;
-  int ipad = 2;
+  int ipad = 128;
   while (ipad < nitems) ipad <<= 1;
   for (int x = nitems + tid; x < ipad; x += PLAN_THREADS) keys[x] = 0xffffffffu;
   __syncthreads();
 
-  // bitonic sort of the item keys, ascending.  Pair index i maps to the
-  // elements lo, lo | jj; for jj < 64 the 64 pairs of one wave stay inside
-  // one run of 128 elements, so those passes only order the wave's own LDS
-  // accesses, and the workgroup synchronises once per merge level and after
-  // every wider pass.
-  for (int kk = 2; kk <= ipad; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < (ipad >> 1); i += PLAN_THREADS) {
-        const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
-        const int hi = lo | jj;
-        const uint32_t a = keys[lo], b = keys[hi];
-        const bool asc = (lo & kk) == 0;
-        if ((a > b) == asc) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      if (jj >= 64) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+  // bitonic sort of the item keys, ascending.  Merge levels 2 .. 128 stay
+  // inside 128-key chunks: each wave sorts its chunks in registers.  Every
+  // later level kk runs its stages of distance >= 128 over the whole list in
+  // LDS rounds (sort_round, up to three stages each) and the rest inside the
+  // chunks again, so that the workgroup synchronises only between those.
+  const int nchunks = ipad >> 7;
+  for (int c = wave; c < nchunks; c += PLAN_THREADS / 64) {
+    uint32_t v[2] = {keys[128 * c + lane], keys[128 * c + 64 + lane]};
+    static_for<1, 8>([&](auto kl) {
+      constexpr int KK = 1 << decltype(kl)::value;
+      chunk_stages<KK / 2>(v, lane, 128 * c, KK);
+    });
+    keys[128 * c + lane] = v[0];
+    keys[128 * c + 64 + lane] = v[1];
+  }
+  __syncthreads();
+  for (int kk = 256; kk <= ipad; kk <<= 1) {
+    int jj = kk >> 1;
+    for (; jj >= 512; jj >>= 3) sort_round<3>(keys, ipad, kk, jj, tid);
+    if (jj == 256) sort_round<2>(keys, ipad, kk, 256, tid);
+    else if (jj == 128) sort_round<1>(keys, ipad, kk, 128, tid);
+    for (int c = wave; c < nchunks; c += PLAN_THREADS / 64) {
+      uint32_t v[2] = {keys[128 * c + lane], keys[128 * c + 64 + lane]};
+      chunk_stages<64>(v, lane, 128 * c, kk);
+      keys[128 * c + lane] = v[0];
+      keys[128 * c + 64 + lane] = v[1];
     }
     __syncthreads();
   }
