@@ -448,9 +448,10 @@ static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
-// Merge of split tiles (one workgroup per split slot), run after the attention
-// launch (which also resets the queue counter here): the two parts'
-// partial results combine as in the online softmax (GSRS A.1): with
+// Merge of split tiles (BLK/32 workgroups per split slot, 32 query rows each),
+// run after the attention launch (this launch also resets the queue counter):
+// the two parts' partial results combine as in the online softmax (GSRS A.1):
+// with
 // m = max(m0, m1) and weights a_p = 2^(m_p - m), O = (a0 O0 + a1 O1) /
 // (a0 l0 + a1 l1) and LSE = (m + log2(a0 l0 + a1 l1)) ln 2.  Part 0 and part 1
 // enter the formula in that order whichever finished last, so the result does
@@ -462,9 +463,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
                                                         int n, int64_t stride_head, int64_t stride_token,
                                                         bf16_t* __restrict__ o, float* __restrict__ lse,
                                                         uint32_t* __restrict__ tile_counter) {
-  const int s = blockIdx.x;
+  // a thread takes 4 output columns of NP rows and issues all its loads
+  // before any arithmetic
+  constexpr int WPS = BLK / 32;      // workgroups per slot
+  constexpr int CPR = D / 4;         // 4-float chunks per row
+  constexpr int RPP = 256 / CPR;     // rows per pass
+  constexpr int NP = 32 / RPP;       // passes
+  const int s = blockIdx.x / WPS;
+  const int r0 = (blockIdx.x % WPS) * 32;
   // the attention launch has finished: reset the queue for the next call
-  if (s == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     atomicExch(&tile_counter[0], 0u);
     atomicExch(&tile_counter[1], 0u);
   }
@@ -474,21 +482,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   constexpr int PART = BLK * D + 2 * BLK;
   const float* p0 = partial + (int64_t)s * 2 * PART;
   const float* p1 = p0 + PART;
-  for (int x = threadIdx.x; x < BLK * (D / 4); x += 256) {
-    const int q = x / (D / 4), c = (x % (D / 4)) * 4;
-    const int tok = order[i * BLK + q];
-    if (tok < 0) continue;
-    const float m0 = p0[BLK * D + q], m1 = p1[BLK * D + q];
-    const float m = fmaxf(m0, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m0 - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-    const float l = a0 * p0[BLK * D + BLK + q] + a1 * p1[BLK * D + BLK + q];
+  const int c = (threadIdx.x % CPR) * 4;
+  int tok[NP];
+  float m0[NP], m1[NP], l0[NP], l1[NP];
+  f32x4 x0[NP], x1[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int q = r0 + j * RPP + threadIdx.x / CPR;
+    tok[j] = order[i * BLK + q];
+    m0[j] = p0[BLK * D + q];
+    m1[j] = p1[BLK * D + q];
+    l0[j] = p0[BLK * D + BLK + q];
+    l1[j] = p1[BLK * D + BLK + q];
+    x0[j] = *reinterpret_cast<const f32x4*>(p0 + q * D + c);
+    x1[j] = *reinterpret_cast<const f32x4*>(p1 + q * D + c);
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (tok[j] < 0) continue;
+    const float m = fmaxf(m0[j], m1[j]);
+    const float a0 = __builtin_amdgcn_exp2f(m0[j] - m), a1 = __builtin_amdgcn_exp2f(m1[j] - m);
+    const float l = a0 * l0[j] + a1 * l1[j];
     const float inv = 1.0f / l;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p0 + q * D + c);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(p1 + q * D + c);
-    const u32x2 w = {pack_bf16x2((a0 * x0[0] + a1 * x1[0]) * inv, (a0 * x0[1] + a1 * x1[1]) * inv),
-                     pack_bf16x2((a0 * x0[2] + a1 * x1[2]) * inv, (a0 * x0[3] + a1 * x1[3]) * inv)};
-    *reinterpret_cast<u32x2*>(o + (int64_t)h * stride_head + (int64_t)tok * stride_token + c) = w;
-    if (c == 0 && lse != nullptr) lse[(int64_t)h * n + tok] = (m + __log2f(l)) * 0.69314718055994531f;
+    const u32x2 w = {pack_bf16x2((a0 * x0[j][0] + a1 * x1[j][0]) * inv, (a0 * x0[j][1] + a1 * x1[j][1]) * inv),
+                     pack_bf16x2((a0 * x0[j][2] + a1 * x1[j][2]) * inv, (a0 * x0[j][3] + a1 * x1[j][3]) * inv)};
+    *reinterpret_cast<u32x2*>(o + (int64_t)h * stride_head + (int64_t)tok[j] * stride_token + c) = w;
+    if (c == 0 && lse != nullptr) lse[(int64_t)h * n + tok[j]] = (m + __log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -564,7 +583,7 @@ int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, 
 
 template <int D, int BLK>
 static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
-  const int grid = rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
+  const int grid = (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS) * (BLK / 32);
   attn_merge_kernel<D, BLK><<<grid, 256, 0, stream>>>(a.partial, a.plan_meta, a.order, rows, a.nb, a.n,
                                                       a.stride_head, a.stride_token, a.o, a.lse,
                                                       a.tile_counter);
