@@ -529,58 +529,6 @@ int attn_blocks_per_cu(int d, int block) {
   return b < 1 ? 1 : b;
 }
 
-// GSRS S5.3 phase 2 (one workgroup per (head, query block) row): the
-// importance of kept block j is the mean over the block's queries of
-// exp(block LSE - row LSE), the share of each query's attention weight that
-// falls on j's keys; blocks not kept get 0.  Rows sum to 1.
-template <int BLK>
-__global__ __launch_bounds__(256) void block_importance_kernel(const int32_t* __restrict__ order,
-                                                              const int32_t* __restrict__ row_ptr,
-                                                              const int32_t* __restrict__ col_idx,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ block_lse, int n, int nb,
-                                                              float* __restrict__ importance) {
-  // The row's block LSEs are one contiguous run of (kept pairs) x BLK floats;
-  // the workgroup streams it with 16-byte loads, BLK/4 lanes per pair, and
-  // reduces each pair inside its lane group.
-  constexpr int LPP = BLK / 4;          // lanes per pair
-  constexpr int PPI = 256 / LPP;        // pairs per pass
-  __shared__ float row_lse[BLK];
-  const int t = blockIdx.x, h = t / nb, i = t - h * nb;
-  const int tid = threadIdx.x;
-  for (int qq = tid; qq < BLK; qq += 256) {
-    const int tok = order[i * BLK + qq];
-    row_lse[qq] = tok >= 0 ? lse[(int64_t)h * n + tok] : INFINITY;  // exp(x - inf) = 0 for slots past N
-  }
-  float* out = importance + (int64_t)t * nb;
-  for (int j = tid; j < nb; j += 256) out[j] = 0.f;
-  __syncthreads();
-  const float inv_rows = 1.0f / (float)min(BLK, n - i * BLK);
-  const int c0 = row_ptr[t], c1 = row_ptr[t + 1];
-  const int g = tid / LPP, r = (tid % LPP) * 4;
-  for (int c = c0 + g; c < c1; c += PPI) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(block_lse + (int64_t)c * BLK + r);
-    float acc = expf(x[0] - row_lse[r]) + expf(x[1] - row_lse[r + 1]) + expf(x[2] - row_lse[r + 2]) +
-                expf(x[3] - row_lse[r + 3]);
-#pragma unroll
-    for (int off = LPP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (tid % LPP == 0) out[col_idx[c]] = acc * inv_rows;
-  }
-}
-
-int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, const int32_t* row_ptr,
-                            const int32_t* col_idx, const float* lse, const float* block_lse,
-                            float* importance, hipStream_t stream) {
-  const int rows = p.num_heads * nb;
-  if (p.block == 128)
-    block_importance_kernel<128><<<rows, 256, 0, stream>>>(order, row_ptr, col_idx, lse, block_lse, p.seq_len, nb,
-                                                           importance);
-  else
-    block_importance_kernel<64><<<rows, 256, 0, stream>>>(order, row_ptr, col_idx, lse, block_lse, p.seq_len, nb,
-                                                          importance);
-  return record_hip_error(hipGetLastError(), "block_importance launch");
-}
-
 template <int D, int BLK>
 static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
   const int grid = (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS) * (BLK / 32);
