@@ -14,6 +14,7 @@
 namespace fva {
 
 constexpr int PLAN_THREADS = 1024;
+constexpr int FILL_WGS_MAX = 1024;  // CSR fill workgroups of the plan launch
 
 __device__ __forceinline__ int refill_count(int k, int nb, int f) {
   return k + (int)min((int64_t)(nb - k), (int64_t)k * f / 1000);
@@ -100,7 +101,7 @@ __device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int bas
 // kept blocks, then the rest), since no ordering can balance a single item
 // larger than the mean.  Split tiles get slots 0, 1, ... in tile-id order.
 // Fewer than 2 * split_s tiles can qualify, and split_s <= FVA_MAX_SPLITS / 2.
-__global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
+__device__ __forceinline__ void plan_scan(
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ head_refill, int rows, int nb,
     int refill_per_mille, int split_s,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_count_final,
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
     uint32_t* __restrict__ tile_counter) {
   // at most FVA_MAX_TILES + FVA_MAX_SPLITS - 1 items, padded to a power of two
   static_assert(FVA_MAX_SPLITS <= FVA_MAX_TILES, "item list fits the padded sort");
-  __shared__ uint32_t keys[2 * FVA_MAX_TILES];
+  extern __shared__ uint32_t keys[];  // sized by the launch to the padded item count
   __shared__ int32_t wave_tot[PLAN_THREADS / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -222,47 +223,95 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scan_kernel(
   }
 }
 
-// One workgroup per row: mark the first k'_i ranked key blocks in an LDS
-// bitmap, then emit their ids in ascending order at the row's CSR offset.
-__global__ __launch_bounds__(256) void plan_fill_kernel(
-    const int16_t* __restrict__ ranked, const int32_t* __restrict__ row_ptr, int nb,
-    int32_t* __restrict__ col_idx) {
-  __shared__ uint32_t bits[FVA_MAX_BLOCKS / 32];
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int start = row_ptr[row];
-  const int kp = row_ptr[row + 1] - start;
-  int32_t* out = col_idx + start;
-  if (kp >= nb) {
-    for (int j = tid; j < nb; j += 256) out[j] = j;
-    return;
-  }
-  const int nwords = (nb + 31) >> 5;
-  for (int w = tid; w < nwords; w += 256) bits[w] = 0u;
-  __syncthreads();
-  const int16_t* rk = ranked + (int64_t)row * nb;
-  for (int r = tid; r < kp; r += 256) {
-    const int j = rk[r];
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  if (tid < 64) {
-    // each lane owns words lane, lane+64, ... ; nwords <= 64 for nb <= 2048
-    const uint32_t word = (tid < nwords) ? bits[tid] : 0u;
-    const int cnt = __popc(word);
-    int incl = cnt;
+// CSR column fill, four rows per workgroup (a quarter of it per row): mark
+// the first k'_i ranked key blocks in an LDS bitmap, then emit their ids in
+// ascending order at the row's CSR offset.  The workgroup computes the
+// offsets itself, the sum of k' over the rows before its first row (the same
+// integers the scan adds), so it does not wait for the scan.
+__device__ __forceinline__ void plan_fill(const int16_t* __restrict__ ranked, const int32_t* __restrict__ row_count,
+                                          const int32_t* __restrict__ head_refill, int rows, int nb,
+                                          int refill_per_mille, int first, int last,
+                                          int32_t* __restrict__ col_idx) {
+  __shared__ uint32_t bits[4][FVA_MAX_BLOCKS / 32];
+  __shared__ int32_t wave_sum[PLAN_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qr = tid >> 8, qt = tid & 255;  // quarter (row) and thread in it
+  auto kept = [&](int r) {
+    return refill_count(row_count[r], nb, row_refill(head_refill, r, nb, refill_per_mille));
+  };
+  int part = 0;
+  for (int r = tid; r < first; r += PLAN_THREADS) part += kept(r);
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += y;
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+  if (lane == 0) wave_sum[wave] = part;
+  __syncthreads();
+  int base = 0;  // CSR offset of row r0 below
+#pragma unroll
+  for (int w = 0; w < PLAN_THREADS / 64; ++w) base += wave_sum[w];
+  const int nwords = (nb + 31) >> 5;
+  for (int r0 = first; r0 < last; r0 += 4) {
+    const int row = r0 + qr;
+    int start = base, kp = 0;
+    for (int r = r0; r < r0 + 4 && r < rows; ++r) {
+      const int k = kept(r);
+      if (r < row) start += k;
+      if (r == row) kp = k;
+      base += k;
     }
-    int pos = incl - cnt;
-    uint32_t w = word;
-    while (w) {
-      const int b = __ffs(w) - 1;
-      out[pos++] = tid * 32 + b;
-      w &= w - 1;
+    const bool live = row < last;
+    const bool full = kp >= nb;
+    for (int w = qt; w < nwords; w += 256) bits[qr][w] = 0u;
+    __syncthreads();
+    if (live && !full) {
+      const int16_t* rk = ranked + (int64_t)row * nb;
+      for (int r = qt; r < kp; r += 256) {
+        const int j = rk[r];
+        atomicOr(&bits[qr][j >> 5], 1u << (j & 31));
+      }
     }
+    __syncthreads();
+    int32_t* out = col_idx + start;
+    if (live && full) {
+      for (int j = qt; j < nb; j += 256) out[j] = j;
+    } else if (live && qt < 64) {
+      // each lane owns one word; nwords <= 64 for nb <= 2048
+      const uint32_t word = (qt < nwords) ? bits[qr][qt] : 0u;
+      const int cnt = __popc(word);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (qt >= off) incl += y;
+      }
+      int pos = incl - cnt;
+      uint32_t w = word;
+      while (w) {
+        const int bb = __ffs(w) - 1;
+        out[pos++] = qt * 32 + bb;
+        w &= w - 1;
+      }
+    }
+    __syncthreads();  // every quarter is done with its bitmap
+  }
+}
+
+// One launch: workgroup 0 runs the scans, the split rule and the sorted work
+// list; workgroups 1, 2, ... fill the CSR columns of four rows each.
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
+    const int16_t* __restrict__ ranked, const int32_t* __restrict__ row_count,
+    const int32_t* __restrict__ head_refill, int rows, int nb, int refill_per_mille, int split_s,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ head_count_final,
+    int32_t* __restrict__ work_order, int32_t* __restrict__ plan_meta, uint32_t* __restrict__ tile_counter) {
+  if (blockIdx.x == 0) {
+    plan_scan(row_count, head_refill, rows, nb, refill_per_mille, split_s, row_ptr, head_count_final, work_order,
+              plan_meta, tile_counter);
+  } else {
+    // fill workgroup f of F takes the rows [f * per, (f + 1) * per), per a
+    // multiple of four
+    const int nf = (int)gridDim.x - 1, f = (int)blockIdx.x - 1;
+    const int per = ((rows + nf - 1) / nf + 3) & ~3;
+    const int first = min(rows, f * per);
+    plan_fill(ranked, row_count, head_refill, rows, nb, refill_per_mille, first, min(rows, first + per), col_idx);
   }
 }
 
@@ -271,14 +320,15 @@ int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked
                 int32_t* col_idx, int32_t* head_count_final, int32_t* work_order,
                 int32_t* plan_meta, uint32_t* tile_counter, hipStream_t stream) {
   const int rows = p.num_heads * nb;
-  plan_scan_kernel<<<1, PLAN_THREADS, 0, stream>>>(row_count, head_refill, rows, nb,
-                                                   p.refill_per_mille, split_s,
-                                                   row_ptr, head_count_final, work_order, plan_meta,
-                                                   tile_counter);
-  int st = record_hip_error(hipGetLastError(), "plan_scan launch");
-  if (st) return st;
-  plan_fill_kernel<<<rows, 256, 0, stream>>>(ranked, row_ptr, nb, col_idx);
-  return record_hip_error(hipGetLastError(), "plan_fill launch");
+  // the sort's LDS: the item count padded to a power of two (>= 128)
+  const int cap = rows + (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS);
+  int ipad = 128;
+  while (ipad < cap) ipad <<= 1;
+  const int fill_wgs = (rows + 3) / 4 < FILL_WGS_MAX ? (rows + 3) / 4 : FILL_WGS_MAX;
+  plan_kernel<<<1 + fill_wgs, PLAN_THREADS, ipad * sizeof(uint32_t), stream>>>(ranked, row_count, head_refill, rows, nb,
+                                                               p.refill_per_mille, split_s, row_ptr, col_idx,
+                                                               head_count_final, work_order, plan_meta, tile_counter);
+  return record_hip_error(hipGetLastError(), "plan launch");
 }
 
 }  // namespace fva
