@@ -235,7 +235,8 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
 // ---------------------------------------------------------------------------
 // 3. Ranking and cutoff.  One wave per (query block i, head h) row at a time,
 // SEL_ROWS consecutive rows per wave and four waves per workgroup; the sort
-// and the scan use no LDS and no barriers:
+// and the scan use no LDS and no barriers (rows of more than 256 blocks take
+// two waves each, see sort_desc_rows):
 //   - keys (orderable(s_j) << 32) | (2^32-1-j), element x = 64e + lane held
 //     in register e of the lane, sorted descending by a bitonic network
 //     (strides below 64 between lanes, larger strides between registers):
@@ -361,6 +362,155 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
   return max(kp, min(k_min, nb));
 }
 
+// Rows of more than 256 blocks are ranked by W = 2 waves together (one wave
+// alone would take 16 or 32 keys per lane through the whole network), two
+// rows per workgroup.  Slot x = 64 (EL v + e) + lane of a row is register e
+// of lane `lane` of the row's wave v (v = 0 .. W-1, EL = E / W keys per
+// lane); the bitonic stages of stride below 64 exchange between lanes,
+// strides 64 .. 32 EL between registers, and stride 64 EL -- the widest
+// stage of the last merge level -- between the row's two waves through LDS.
+constexpr int RANK_WAVES = 2;  // waves per row for rows of more than 256 blocks
+
+template <int EL>
+struct RowRankLds {
+  uint64_t xbuf[RANK_WAVES * EL * 64];
+  uint64_t wave_total[RANK_WAVES];
+  int wave_count[RANK_WAVES];
+  uint32_t top;
+};
+
+template <int EL>
+__device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, int v, uint64_t* xbuf) {
+  constexpr int LOG = __builtin_ctz(64 * EL * RANK_WAVES);
+  const int x0 = v * EL * 64 + lane;  // slot of register 0
+  static_for<1, LOG + 1>([&](auto kl) {
+    constexpr int KK = 1 << decltype(kl)::value;
+    static_for<0, decltype(kl)::value>([&](auto jl) {
+      constexpr int JJ = KK >> (decltype(jl)::value + 1);
+      if constexpr (JJ >= 64 * EL) {
+        constexpr int WJ = JJ / (64 * EL);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) xbuf[(v * EL + e) * 64 + lane] = key[e];
+        __syncthreads();
+        const bool lower = (v & WJ) == 0;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          const bool desc = ((x0 + e * 64) & KK) == 0;
+          const uint64_t a = key[e], b = xbuf[((v ^ WJ) * EL + e) * 64 + lane];
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          key[e] = (lower == desc) ? hi : lo;
+        }
+        __syncthreads();
+      } else if constexpr (JJ >= 64) {
+        constexpr int JE = JJ / 64;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          if ((e & JE) == 0) {
+            const bool desc = ((x0 + e * 64) & KK) == 0;
+            const uint64_t a = key[e], b = key[e | JE];
+            if ((a < b) == desc) {
+              key[e] = b;
+              key[e | JE] = a;
+            }
+          }
+        }
+      } else {
+        const bool lower = (lane & JJ) == 0;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          const bool desc = ((x0 + e * 64) & KK) == 0;
+          const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          key[e] = (lower == desc) ? hi : lo;
+        }
+      }
+    });
+  });
+}
+
+// select_row for one row ranked by RANK_WAVES waves (same keys, weights,
+// target and count; the weights' inclusive scan runs per wave and is carried
+// across the row's waves in slot order).  `live_row` is false for the second
+// row slot of the last workgroup when the row count is odd: its waves take
+// part in the barriers only.
+template <int EL>
+__device__ __forceinline__ int select_row_waves(const float* __restrict__ scores, int nb, int row, bool live_row,
+                                                float top_p, int k_min, int16_t* __restrict__ ranked, int lane,
+                                                int v, RowRankLds<EL>& sh) {
+  const float* s = scores + (int64_t)row * nb;
+  const int x0 = v * EL * 64 + lane;
+  uint64_t key[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    const int x = x0 + e * 64;
+    key[e] = (live_row && x < nb) ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x))
+                                  : 0ull;
+  }
+  sort_desc_rows<EL>(key, lane, v, sh.xbuf);
+
+  if (live_row) {
+    int16_t* rk = ranked + (int64_t)row * nb;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int x = x0 + e * 64;
+      if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
+    }
+  }
+
+  int kp;
+  const float p = top_p;
+  if (p >= 1.0f) {
+    kp = nb;
+  } else if (!(p > 0.0f)) {
+    kp = 0;
+  } else {
+    if (v == 0 && lane == 0) sh.top = (uint32_t)(key[0] >> 32);
+    __syncthreads();
+    const double smax = (double)from_orderable(sh.top);
+    uint64_t prefix[EL];
+    bool live[EL];
+    uint64_t carry = 0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int x = x0 + e * 64;
+      const double sr = (double)from_orderable((uint32_t)(key[e] >> 32));
+      live[e] = live_row && x < nb;
+      uint64_t incl = live[e] ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t y = shfl_up_u64(incl, off);
+        if (lane >= off) incl += y;
+      }
+      prefix[e] = carry + incl;
+      const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+      const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63);
+      carry += ((uint64_t)thi << 32) | tlo;
+    }
+    if (lane == 0) sh.wave_total[v] = carry;
+    __syncthreads();
+    uint64_t before = 0, total = 0;
+#pragma unroll
+    for (int u = 0; u < RANK_WAVES; ++u) {
+      const uint64_t t = sh.wave_total[u];
+      total += t;
+      if (u < v) before += t;
+    }
+    const uint64_t tint = (uint64_t)ceil((double)p * (double)total);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) cnt += (live[e] && before + prefix[e] < tint) ? 1 : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) sh.wave_count[v] = cnt;
+    __syncthreads();
+    int c = 1;
+#pragma unroll
+    for (int u = 0; u < RANK_WAVES; ++u) c += sh.wave_count[u];
+    kp = min(nb, c);
+  }
+  return max(kp, min(k_min, nb));
+}
+
 // Re-selection inside an evaluated set (growing sparsity with reduced
 // search): the row's evaluated blocks (its CSR entries) are ranked by their
 // precise importance, descending, equal values by lower id, and the other
@@ -443,8 +593,23 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     vt_relayout_block<D>(vr, w % vr.nb, w / vr.nb, tok);
     return;
   }
-  __shared__ int wg_sum;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (E >= 8) {
+    // two rows per workgroup, RANK_WAVES waves per row
+    constexpr int RPW = 4 / RANK_WAVES;
+    __shared__ RowRankLds<E / RANK_WAVES> sh[RPW];
+    const int slot = wave / RANK_WAVES, v = wave % RANK_WAVES;
+    const int row = blockIdx.x * RPW + slot;
+    const bool live_row = row < rows;
+    const int ki = select_row_waves<E / RANK_WAVES>(scores, nb, live_row ? row : 0, live_row, top_p, k_min,
+                                                    ranked, lane, v, sh[slot]);
+    if (live_row && v == 0 && lane == 0) {
+      row_count[row] = ki;
+      atomicAdd(&head_count[row / nb], ki);
+    }
+    return;
+  }
+  __shared__ int wg_sum;
   const int first = blockIdx.x * 4 * SEL_ROWS;
   const int last = min(rows, first + 4 * SEL_ROWS) - 1;
   const bool one_head = first / nb == last / nb;  // the common case: pool the workgroup's sum
@@ -561,10 +726,12 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   // workgroups would hold the score tiles' 66 KB of LDS each)
   const int rows = p.num_heads * nb;
   const VRelayout vr{(const bf16_t*)v, p.stride_head, p.stride_token, order, vt, p.block, nb, p.seq_len};
-  const int sel_wgs = (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
-  const int grid = sel_wgs + rows;
   int e = 1;
   while (64 * e < nb) e <<= 1;
+  // ranking workgroups: four rows each (one wave per row), or two rows each
+  // (two waves per row) when a row has more than 256 blocks (E >= 8)
+  const int sel_wgs = e >= 8 ? (rows + 1) / 2 : (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
+  const int grid = sel_wgs + rows;
 #define FVA_SELECT(E_)                                                                               \
   do {                                                                                               \
     if (p.head_dim == 128)                                                                           \
