@@ -1,0 +1,107 @@
+"""GPU: the problem options the workload tests leave at their defaults.
+
+- an explicit softmax scale (the routing's block scores and the attention
+  both use it) against the oracle at that scale;
+- the attention call without its LSE output gives the same O bit for bit;
+- token rows padded past d (stride_token > d, as a fused QKV projection
+  leaves them) give the same outputs as contiguous tensors, and nothing is
+  written into the padding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import adaptive_block_sparse_fva_amd as F
+import oracle as O
+from gpu_helpers import (LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, S_REL, device_inputs, f64_inputs,
+                         problem_for, run_chain, say)
+from synth import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+SCALES = [("two_head", 0.05), ("two_head", 0.2), ("tiny", 0.3)]
+
+
+@pytest.mark.parametrize("name,scale", SCALES, ids=[f"{n}-s{s}" for n, s in SCALES])
+def test_explicit_softmax_scale(name, scale):
+    wl = WORKLOADS[name]
+    p = wl.top_p[0]
+    say(f"[gpu] sm_scale {scale} on {name}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, p, sm_scale=scale), q, k, v)
+    H, nb = wl.num_heads, res["nb"]
+    q64, k64, v64 = f64_inputs(inp)
+    order = O.token_order(wl.grid, wl.tile_hw)
+    s64 = O.block_scores(O.pool(q64, order, wl.block), O.pool(k64, order, wl.block), scale)
+    err = np.abs(res["scores"].astype(np.float64) - s64).max()
+    assert err <= S_REL * np.abs(s64).max(), f"score error {err}"
+    S32 = res["scores"]
+    for r in range(H * nb):
+        h, i = divmod(r, nb)
+        np.testing.assert_array_equal(res["ranked"][r], O.ranking(S32[h, i]), err_msg=f"row {r}")
+    rc, hc = O.select_counts(S32, p, wl.k_min)
+    np.testing.assert_array_equal(res["row_count"], rc)
+    np.testing.assert_array_equal(res["head_count"], hc)
+    pl = O.plan(S32, rc, wl.refill_per_mille)
+    np.testing.assert_array_equal(res["row_ptr"], pl["row_ptr"])
+    np.testing.assert_array_equal(res["col_idx"], pl["col_idx"])
+    o_ref, lse_ref = O.masked_attention(q64, k64, v64, order, wl.block, pl["row_ptr"], pl["col_idx"], scale)
+    do = np.abs(res["o"] - o_ref)
+    dl = np.abs(res["lse"] - lse_ref)
+    say(f"  O max-abs {do.max():.3e} mean-abs {do.mean():.3e}; LSE max-abs {dl.max():.3e}")
+    assert do.max() <= O_MAX_ABS and do.mean() <= O_MEAN_ABS and dl.max() <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("name", ["two_head", "rank480p"])
+def test_lse_output_is_optional(name):
+    wl = WORKLOADS[name]
+    say(f"[gpu] attention without LSE on {name}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    prob = problem_for(wl, wl.top_p[0])
+    buf, with_lse = run_chain(prob, q, k, v)
+    buf.o.zero_()
+    buf.attn(q, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.o.float().cpu(), torch.from_numpy(with_lse["o"]).float())
+
+
+PADDED = [
+    # name, heads, d, grid, block, p, k_min, pad
+    ("two_head", None, None, None, None, None, None, 8),
+    ("d64_ragged", 3, 64, (3, 9, 11), 64, 0.8, 2, 24),
+]
+
+
+@pytest.mark.parametrize("case", PADDED, ids=[c[0] for c in PADDED])
+def test_padded_token_rows(case):
+    name, H, d, grid, block, p, kmin, pad = case
+    wl = WORKLOADS[name] if H is None else Workload(name, H, d, grid, block, (p,), kmin, 0, seed=53,
+                                                    heads="lograndom")
+    p = wl.top_p[0]
+    say(f"[gpu] token rows padded by {pad} on {name}")
+    inp = make_inputs(wl, cache=False) if H is not None else make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, ref = run_chain(problem_for(wl, p), q, k, v)
+    Hh, N, dd = q.shape
+    width = dd + pad
+
+    def padded(x):
+        t = torch.full((Hh, N, width), float("nan"), dtype=torch.bfloat16, device="cuda")
+        t[:, :, :dd] = x
+        return t
+
+    qp, kp, vp = padded(q), padded(k), padded(v)
+    prob = problem_for(wl, p, stride_head=N * width, stride_token=width)
+    buf = F.Buffers.allocate(prob)
+    sentinel = torch.tensor(12345.0, dtype=torch.bfloat16)
+    buf.o = torch.full((Hh, N, width), sentinel.item(), dtype=torch.bfloat16, device="cuda")
+    buf.run(qp, kp, vp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(buf.o[:, :, :dd].float().cpu().numpy(), ref["o"])
+    np.testing.assert_array_equal(buf.lse.cpu().numpy(), ref["lse"].astype(np.float32))
+    np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
+    assert bool((buf.o[:, :, dd:] == sentinel.item()).all()), "padding was written"
