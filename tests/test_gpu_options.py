@@ -5,7 +5,8 @@
 - the attention call without its LSE output gives the same O bit for bit;
 - token rows padded past d (stride_token > d, as a fused QKV projection
   leaves them) give the same outputs as contiguous tensors, and nothing is
-  written into the padding.
+  written into the padding;
+- extreme values: very sharp logits and all-zero queries.
 """
 
 import numpy as np
@@ -105,3 +106,55 @@ def test_padded_token_rows(case):
     np.testing.assert_array_equal(buf.lse.cpu().numpy(), ref["lse"].astype(np.float32))
     np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
     assert bool((buf.o[:, :, dd:] == sentinel.item()).all()), "padding was written"
+
+
+def _scaled_bits(bits: np.ndarray, pow2: int) -> np.ndarray:
+    """bf16 bits times 2^pow2, exactly (only the exponent changes)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** pow2)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+VALUES = [("sharp_logits", 3), ("zero_queries", None)]
+
+
+@pytest.mark.parametrize("name,pow2", VALUES, ids=[c[0] for c in VALUES])
+def test_extreme_values(name, pow2):
+    """Q and K times 8 (logits x 64: the running maximum moves by far more than
+    the rescale threshold, most weights underflow), and all-zero queries
+    (every block score ties at 0, so the ranking is by block id alone, and
+    every kept key has the same weight)."""
+    import dataclasses
+
+    from test_gpu_parity import check_attention, check_routing_and_plan
+
+    wl = WORKLOADS["two_head"]
+    p = wl.top_p[0]
+    say(f"[gpu] {name}")
+    inp = make_inputs(wl)
+    if pow2 is None:
+        inp = dataclasses.replace(inp, q=np.zeros_like(inp.q))
+    else:
+        inp = dataclasses.replace(inp, q=_scaled_bits(inp.q, pow2), k=_scaled_bits(inp.k, pow2))
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, p), q, k, v)
+    check_routing_and_plan(wl, inp, res, p, wl.refill_per_mille)
+    if pow2 is None:
+        check_attention(wl, inp, res, label=name)
+    else:
+        # O to the usual bar; the LSE to a bar relative to its size: with
+        # logits of magnitude 10^2 .. 10^4 the fp32 dot products themselves
+        # carry errors of ~1e-6 relative (d = 128 terms of up to 10^5 each),
+        # and a sharp softmax's LSE is its largest logit
+        q64, k64, v64 = f64_inputs(inp)
+        order = O.token_order(wl.grid, wl.tile_hw)
+        o_ref, lse_ref = O.masked_attention(q64, k64, v64, order, wl.block, res["row_ptr"], res["col_idx"],
+                                            1.0 / np.sqrt(wl.head_dim))
+        do = np.abs(res["o"] - o_ref)
+        dl = np.abs(res["lse"] - lse_ref)
+        rel = dl / (1e-3 + 2.0 ** -16 * np.abs(lse_ref))
+        say(f"  O max-abs {do.max():.3e} mean-abs {do.mean():.3e}; LSE max-abs {dl.max():.3e} "
+            f"(|LSE| up to {np.abs(lse_ref).max():.3e}, worst error / bar {rel.max():.2f})")
+        assert do.max() <= O_MAX_ABS and do.mean() <= O_MEAN_ABS
+        assert rel.max() <= 1.0
+    if pow2 is None:
+        np.testing.assert_array_equal(res["ranked"], np.tile(np.arange(res["nb"]), (wl.num_heads * res["nb"], 1)))
