@@ -228,7 +228,9 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
  *                denominator) in the workspace, and a second kernel merges
  *                them and writes that tile's o and lse.
  *   tile_counter device uint32 [2], must be {0, 0} on entry (fva_plan leaves
- *                it so); the kernel leaves it {0, 0} again on exit.
+ *                it so); the kernel leaves it {0, 0} again on exit.  Calls
+ *                that may run at the same time (other streams) need their
+ *                own tile_counter and workspace.
  *   o            device bf16 [H][N][d] (strided like q), written.
  *   lse          device float [H][N] or NULL, written: natural-log
  *                log-sum-exp of each query's kept logits.
