@@ -12,6 +12,7 @@ from .fva import (  # noqa: F401
     GsrsSchedule,
     Problem,
     attn_workgroups,
+    compute_units,
     balance,
     balance_params,
     block_importance,

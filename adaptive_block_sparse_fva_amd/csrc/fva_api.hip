@@ -188,6 +188,14 @@ int fva_sizes(const fva_problem* prob, fva_sizes_t* out) {
   return FVA_OK;
 }
 
+int fva_compute_units(int32_t* out) {
+  if (out == nullptr) return FVA_ERR_ARG;
+  const int cus = device_cu_count();
+  if (cus < 1) return record_hip_error(hipErrorNoDevice, "compute unit count");
+  *out = cus;
+  return FVA_OK;
+}
+
 int fva_attn_workgroups(const fva_problem* prob, int32_t* out) {
   int nb = 0;
   if (out == nullptr) return FVA_ERR_ARG;
@@ -227,10 +235,13 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_
   if (!ranked || !row_count || !row_ptr || !col_idx || !head_count_final || !work_order ||
       !plan_meta || !tile_counter)
     return FVA_ERR_ARG;
-  int grid = 0;
-  st = attn_grid(*prob, nb, &grid);
-  if (st) return st;
-  const int split_s = grid < FVA_MAX_SPLITS / 2 ? grid : FVA_MAX_SPLITS / 2;
+  const int cus = device_cu_count();
+  if (cus < 1) return record_hip_error(hipErrorNoDevice, "compute unit count");
+  // a tile is cut when it is heavier than about the mean load of one compute
+  // unit: the two workgroups a unit runs share its throughput, so anything
+  // lighter is absorbed by the heaviest-first queue
+  int split_s = cus / 2 < FVA_MAX_SPLITS / 2 ? cus / 2 : FVA_MAX_SPLITS / 2;
+  if (split_s < 1) split_s = 1;
   return launch_plan(*prob, nb, split_s, ranked, row_count, head_refill, row_ptr, col_idx,
                      head_count_final, work_order, plan_meta, tile_counter, (hipStream_t)stream);
 }

@@ -95,12 +95,13 @@ __device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int bas
 // decision, the heaviest-first work list, queue reset.  Rows (tiles) are at
 // most FVA_MAX_TILES = 16384, work items at most rows + FVA_MAX_SPLITS.
 //
-// Placement on one GPU: a tile whose kept count k' exceeds the
-// mean load a = ceil(sum k' / split_s) of a workgroup by more than half
-// (k' >= 2 and 2 k' > a) is cut into two work items (its first ceil(k'/2)
+// Placement on one GPU: with a = ceil(sum k' / split_s) and split_s = half
+// the compute units (a / 2 is then about the mean load of one unit), a tile
+// with k' >= 2 and 2 k' > a is cut into two work items (its first ceil(k'/2)
 // kept blocks, then the rest), since no ordering can balance a single item
-// larger than the mean.  Split tiles get slots 0, 1, ... in tile-id order.
-// Fewer than 2 * split_s tiles can qualify, and split_s <= FVA_MAX_SPLITS / 2.
+// larger than a unit's mean load.  Split tiles get slots 0, 1, ... in tile-id
+// order.  Fewer than 2 * split_s tiles can qualify, and
+// split_s <= FVA_MAX_SPLITS / 2.
 __device__ __forceinline__ void plan_scan(
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ head_refill, int rows, int nb,
     int refill_per_mille, int split_s,

@@ -49,6 +49,7 @@ FVA_GSRS_REUSE = 3
 EXPORTED = (
     "fva_sizes",
     "fva_attn_workgroups",
+    "fva_compute_units",
     "fva_route",
     "fva_plan",
     "fva_sparse_attn_fwd",
@@ -163,6 +164,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.fva_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.fva_compute_units.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -181,7 +183,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_last_error.argtypes = []
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
-    for name in ("fva_sizes", "fva_attn_workgroups", "fva_route", "fva_plan",
+    for name in ("fva_sizes", "fva_attn_workgroups", "fva_compute_units", "fva_route", "fva_plan",
                  "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_balance",
                  "fva_sasa_refill", "fva_reselect", "fva_gsrs_action", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -226,6 +228,13 @@ def attn_workgroups(prob: Problem) -> int:
     out = ctypes.c_int32(0)
     _check(load_library().fva_attn_workgroups(ctypes.byref(prob), ctypes.byref(out)),
            "fva_attn_workgroups")
+    return int(out.value)
+
+
+def compute_units() -> int:
+    """Compute units of the current device (the count the plan's split rule uses)."""
+    out = ctypes.c_int32(0)
+    _check(load_library().fva_compute_units(ctypes.byref(out)), "fva_compute_units")
     return int(out.value)
 
 

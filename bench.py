@@ -484,6 +484,12 @@ def main():
     lpt = list_schedule_makespan(np.sort(costs)[::-1], workers)
     natural = list_schedule_makespan(costs, workers)
     ideal = costs.sum() / workers
+    # the same per compute unit (its resident workgroups share its throughput,
+    # so a unit behaves like one worker at the unit's rate)
+    cus = F.compute_units()
+    ideal_cu = costs.sum() / cus
+    per_cu = {"planned": round(list_schedule_makespan(it_cost, cus) / ideal_cu, 4),
+              "natural": round(list_schedule_makespan(costs, cus) / ideal_cu, 4)}
 
     # GSRS precise block importance (phase 1 inside the attention call, phase
     # 2 as its own kernel): cost over the plain attention call
@@ -628,7 +634,8 @@ def main():
         "precise_importance": precise,
         "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
                          "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
-                         "natural": round(natural / ideal, 4)},
+                         "natural": round(natural / ideal, 4), "compute_units": cus,
+                         "per_compute_unit": per_cu},
         "dense_reference": dense,
         "balance": balance,
         "gsrs": gsrs,

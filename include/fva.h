@@ -139,6 +139,11 @@ int fva_sizes(const fva_problem* prob, fva_sizes_t* out);
  * unit, at most H*nb).  Queries the device; FVA_ERR_HIP without one. */
 int fva_attn_workgroups(const fva_problem* prob, int32_t* out);
 
+/* Compute units of the current device: the count C that fva_plan's split
+ * rule uses.  Queries the device; FVA_ERR_HIP without one, FVA_ERR_ARG for a
+ * null out. */
+int fva_compute_units(int32_t* out);
+
 /*
  * Routing frontend (FVAttn S3.1; GSRS S5.3, A.4, A.6).
  *   q, k, v     device bf16 [H][N][d] (strided as above), read only.
@@ -192,8 +197,10 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
  *   head_count_final  device int32 [H], written: sum of k'_i per head.
  *   work_order   device int32 [work_order_elems], written: the work items,
  *                entries tile * 2 + part (tile id h*nb + i), longest first,
- *                then tile, then part.  With W = fva_attn_workgroups(),
- *                S = min(W, FVA_MAX_SPLITS / 2) and a = ceil(sum k' / S), a
+ *                then tile, then part.  With C = fva_compute_units(),
+ *                S = min(max(C / 2, 1), FVA_MAX_SPLITS / 2) and
+ *                a = ceil(sum k' / S) (so a / 2 is about the mean load of
+ *                one compute unit), a
  *                tile with k' >= 2 and 2 k' > a is two items: part 0 = its
  *                first ceil(k'/2) kept blocks, part 1 = the rest; any other
  *                tile is one item (part 0, all its blocks).  Splitting only
@@ -204,7 +211,7 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
  *                tile t (its rank among split tiles by tile id) or -1,
  *                [2 + H*nb + s] tile of split slot s (s < ns).
  *   tile_counter device uint32 [2], written: reset to {0, 0}.
- * Queries the device for W (FVA_ERR_HIP without one).
+ * Queries the device for C (FVA_ERR_HIP without one).
  */
 int fva_plan(const fva_problem* prob, const int16_t* ranked,
              const int32_t* row_count, const int32_t* head_refill,

@@ -288,19 +288,20 @@ def plan(scores32: np.ndarray, row_count: np.ndarray, refill_per_mille: int,
     }
 
 
-def work_items(kept: np.ndarray, workgroups: int, max_splits: int = MAX_SPLITS):
+def work_items(kept: np.ndarray, compute_units: int, max_splits: int = MAX_SPLITS):
     """One-GPU placement of the tiles ([FVA] S3.2 adapted to one GPU).
 
-    Tiles much heavier than the mean load of a workgroup cannot be balanced by
-    ordering alone, so each tile with k' >= 2 and 2 k' > ceil(total / S) is
+    A tile heavier than the mean load of one compute unit cannot be balanced
+    by ordering alone, so each tile with k' >= 2 and 2 k' > ceil(total / S) is
     cut into two work items (the first ceil(k'/2) of its kept blocks, then the
-    rest), S = min(workgroups, max_splits // 2).  Returns the work list (entries
+    rest), S = min(max(compute_units // 2, 1), max_splits // 2): ceil(total / S)
+    / 2 is about total / compute_units.  Returns the work list (entries
     tile * 2 + part, longest item first, then tile, then part), the split slot
     of every tile (its rank among the split tiles by tile id, -1 if whole) and
     the number of split tiles.
     """
     kept = np.asarray(kept, dtype=np.int64)
-    S = min(int(workgroups), max_splits // 2)
+    S = min(max(int(compute_units) // 2, 1), max_splits // 2)
     avg = -(-int(kept.sum()) // S)
     split = (kept >= 2) & (2 * kept > avg)
     slot = np.full(len(kept), -1, dtype=np.int64)

@@ -69,7 +69,7 @@ def test_balanced_refill_chain(case):
     np.testing.assert_array_equal(res["row_ptr"], pl["row_ptr"])
     np.testing.assert_array_equal(res["col_idx"], pl["col_idx"])
     np.testing.assert_array_equal(res["head_count_final"], pl["head_count"])
-    work, slot, nsplit = O.work_items(pl["kept"], F.attn_workgroups(prob))
+    work, slot, nsplit = O.work_items(pl["kept"], F.compute_units())
     np.testing.assert_array_equal(res["work_order"], work)
 
     # SASA bookkeeping: the blocks added per rank are the budget's, on the

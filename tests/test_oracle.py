@@ -298,13 +298,25 @@ def test_plan_lpt_order():
 
 
 def test_work_items_hand_example():
-    # k' = [5, 1, 3, 8], 2 workgroups: total 17, mean load ceil(17/2) = 9, so
-    # tiles with 2k' > 9 (tiles 0 and 3) are cut: 5 -> 3 + 2, 8 -> 4 + 4.
+    # k' = [5, 1, 3, 8], 4 compute units: S = 2, total 17, a = ceil(17/2) = 9,
+    # so tiles with 2k' > 9 (tiles 0 and 3) are cut: 5 -> 3 + 2, 8 -> 4 + 4.
     # Items (length, tile, part): (4,3,0) (4,3,1) (3,0,0) (3,2,0) (2,0,1) (1,1,0).
-    order, slot, nsplit = O.work_items(np.array([5, 1, 3, 8]), 2)
+    order, slot, nsplit = O.work_items(np.array([5, 1, 3, 8]), 4)
     np.testing.assert_array_equal(order, [6, 7, 0, 4, 1, 2])
     np.testing.assert_array_equal(slot, [0, -1, -1, 1])
     assert nsplit == 2
+    # 2 compute units: S = 1, a = 17, no tile has 2k' > 17: four whole tiles,
+    # longest first
+    order, slot, nsplit = O.work_items(np.array([5, 1, 3, 8]), 2)
+    np.testing.assert_array_equal(order, [6, 0, 4, 2])
+    np.testing.assert_array_equal(slot, [-1, -1, -1, -1])
+    assert nsplit == 0
+    # 256 compute units (S = 128) and the 480p-share shape: 1,280 tiles of at
+    # most 256 kept blocks, 104,448 in total: a = 816, no tile has 2k' > 816
+    kept = np.full(1280, 38)
+    kept[:256] = 256
+    order, slot, nsplit = O.work_items(kept, 256)
+    assert nsplit == 0 and len(order) == 1280
 
 
 def test_work_items_invariants():
@@ -314,9 +326,9 @@ def test_work_items_invariants():
         kept = rng.integers(1, 200, rows)
         if trial % 3 == 0:
             kept[: rows // 4] = 200  # a heavy head
-        wg = int(rng.integers(1, 700))
-        order, slot, nsplit = O.work_items(kept, wg)
-        S = min(wg, O.MAX_SPLITS // 2)
+        cus = int(rng.integers(1, 1400))
+        order, slot, nsplit = O.work_items(kept, cus)
+        S = min(max(cus // 2, 1), O.MAX_SPLITS // 2)
         assert nsplit < 2 * S and nsplit <= O.MAX_SPLITS
         tiles, parts = order // 2, order % 2
         # every tile once, split tiles twice (parts 0 and 1)
@@ -330,8 +342,9 @@ def test_work_items_invariants():
                           np.where(parts == 0, (kept[tiles] + 1) // 2, kept[tiles] // 2))
         assert length.sum() == kept.sum()
         assert np.all(np.diff(length) <= 0)
-        # with the heavy tiles cut, no item exceeds the mean load per workgroup
-        # unless a single tile is more than twice that mean
+        # with the heavy tiles cut, no item exceeds a = ceil(total / S) (about
+        # twice a compute unit's mean load) unless a single tile is more than
+        # twice a
         mean = -(-kept.sum() // S)
         assert length.max() <= max(mean, (kept.max() + 1) // 2)
 
