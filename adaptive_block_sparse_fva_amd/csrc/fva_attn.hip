@@ -448,8 +448,9 @@ static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
-// Merge of split tiles (BLK/32 workgroups per split slot, 32 query rows each),
-// run after the attention launch (this launch also resets the queue counter):
+// Merge of split tiles (BLK/32 workgroups per split slot, 32 query rows each;
+// groups of them stride over the slots), run after the attention launch
+// (this launch also resets the queue counter):
 // the two parts' partial results combine as in the online softmax (GSRS A.1):
 // with
 // m = max(m0, m1) and weights a_p = 2^(m_p - m), O = (a0 O0 + a1 O1) /
@@ -469,45 +470,48 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   constexpr int CPR = D / 4;         // 4-float chunks per row
   constexpr int RPP = 256 / CPR;     // rows per pass
   constexpr int NP = 32 / RPP;       // passes
-  const int s = blockIdx.x / WPS;
   const int r0 = (blockIdx.x % WPS) * 32;
   // the attention launch has finished: reset the queue for the next call
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     atomicExch(&tile_counter[0], 0u);
     atomicExch(&tile_counter[1], 0u);
   }
-  if (s >= plan_meta[1]) return;
-  const int t = plan_meta[2 + rows + s];
-  const int h = t / nb, i = t - h * nb;
-  constexpr int PART = BLK * D + 2 * BLK;
-  const float* p0 = partial + (int64_t)s * 2 * PART;
-  const float* p1 = p0 + PART;
-  const int c = (threadIdx.x % CPR) * 4;
-  int tok[NP];
-  float m0[NP], m1[NP], l0[NP], l1[NP];
-  f32x4 x0[NP], x1[NP];
+  // split slots in a grid-stride loop: the grid is sized by the device, not
+  // by the number of split tiles, which only the device knows
+  const int ns = plan_meta[1];
+  for (int s = blockIdx.x / WPS; s < ns; s += gridDim.x / WPS) {
+    const int t = plan_meta[2 + rows + s];
+    const int h = t / nb, i = t - h * nb;
+    constexpr int PART = BLK * D + 2 * BLK;
+    const float* p0 = partial + (int64_t)s * 2 * PART;
+    const float* p1 = p0 + PART;
+    const int c = (threadIdx.x % CPR) * 4;
+    int tok[NP];
+    float m0[NP], m1[NP], l0[NP], l1[NP];
+    f32x4 x0[NP], x1[NP];
 #pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int q = r0 + j * RPP + threadIdx.x / CPR;
-    tok[j] = order[i * BLK + q];
-    m0[j] = p0[BLK * D + q];
-    m1[j] = p1[BLK * D + q];
-    l0[j] = p0[BLK * D + BLK + q];
-    l1[j] = p1[BLK * D + BLK + q];
-    x0[j] = *reinterpret_cast<const f32x4*>(p0 + q * D + c);
-    x1[j] = *reinterpret_cast<const f32x4*>(p1 + q * D + c);
-  }
+    for (int j = 0; j < NP; ++j) {
+      const int q = r0 + j * RPP + threadIdx.x / CPR;
+      tok[j] = order[i * BLK + q];
+      m0[j] = p0[BLK * D + q];
+      m1[j] = p1[BLK * D + q];
+      l0[j] = p0[BLK * D + BLK + q];
+      l1[j] = p1[BLK * D + BLK + q];
+      x0[j] = *reinterpret_cast<const f32x4*>(p0 + q * D + c);
+      x1[j] = *reinterpret_cast<const f32x4*>(p1 + q * D + c);
+    }
 #pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    if (tok[j] < 0) continue;
-    const float m = fmaxf(m0[j], m1[j]);
-    const float a0 = __builtin_amdgcn_exp2f(m0[j] - m), a1 = __builtin_amdgcn_exp2f(m1[j] - m);
-    const float l = a0 * l0[j] + a1 * l1[j];
-    const float inv = 1.0f / l;
-    const u32x2 w = {pack_bf16x2((a0 * x0[j][0] + a1 * x1[j][0]) * inv, (a0 * x0[j][1] + a1 * x1[j][1]) * inv),
-                     pack_bf16x2((a0 * x0[j][2] + a1 * x1[j][2]) * inv, (a0 * x0[j][3] + a1 * x1[j][3]) * inv)};
-    *reinterpret_cast<u32x2*>(o + (int64_t)h * stride_head + (int64_t)tok[j] * stride_token + c) = w;
-    if (c == 0 && lse != nullptr) lse[(int64_t)h * n + tok[j]] = (m + __log2f(l)) * 0.69314718055994531f;
+    for (int j = 0; j < NP; ++j) {
+      if (tok[j] < 0) continue;
+      const float m = fmaxf(m0[j], m1[j]);
+      const float a0 = __builtin_amdgcn_exp2f(m0[j] - m), a1 = __builtin_amdgcn_exp2f(m1[j] - m);
+      const float l = a0 * l0[j] + a1 * l1[j];
+      const float inv = 1.0f / l;
+      const u32x2 w = {pack_bf16x2((a0 * x0[j][0] + a1 * x1[j][0]) * inv, (a0 * x0[j][1] + a1 * x1[j][1]) * inv),
+                       pack_bf16x2((a0 * x0[j][2] + a1 * x1[j][2]) * inv, (a0 * x0[j][3] + a1 * x1[j][3]) * inv)};
+      *reinterpret_cast<u32x2*>(o + (int64_t)h * stride_head + (int64_t)tok[j] * stride_token + c) = w;
+      if (c == 0 && lse != nullptr) lse[(int64_t)h * n + tok[j]] = (m + __log2f(l)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -531,7 +535,12 @@ int attn_blocks_per_cu(int d, int block) {
 
 template <int D, int BLK>
 static int launch_merge_t(const AttnArgs& a, int rows, hipStream_t stream) {
-  const int grid = (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS) * (BLK / 32);
+  // one group of BLK/32 workgroups per split slot, up to one group per
+  // compute unit; more split tiles than groups are taken in turn
+  int slots = rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS;
+  const int cus = device_cu_count();
+  if (cus > 0 && cus < slots) slots = cus;
+  const int grid = slots * (BLK / 32);
   attn_merge_kernel<D, BLK><<<grid, 256, 0, stream>>>(a.partial, a.plan_meta, a.order, rows, a.nb, a.n,
                                                       a.stride_head, a.stride_token, a.o, a.lse,
                                                       a.tile_counter);
