@@ -120,6 +120,18 @@ def test_entry_points_reject_null_pointers_without_a_device():
     assert lib.fva_status_string(fva.FVA_ERR_WORKSPACE) == b"workspace too small"
 
 
+def test_compute_units_checks_its_argument_and_needs_a_device():
+    import torch
+    lib = F.load_library()
+    assert lib.fva_compute_units(None) == fva.FVA_ERR_ARG
+    out = ctypes.c_int32(-1)
+    st = lib.fva_compute_units(ctypes.byref(out))
+    if torch.cuda.is_available():
+        assert st == fva.FVA_OK and out.value > 0
+    else:
+        assert st == fva.FVA_ERR_HIP and out.value == -1
+
+
 def test_route_rejects_small_workspace_before_launch():
     lib = F.load_library()
     p = _ok_problem()

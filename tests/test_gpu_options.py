@@ -6,7 +6,8 @@
 - token rows padded past d (stride_token > d, as a fused QKV projection
   leaves them) give the same outputs as contiguous tensors, and nothing is
   written into the padding;
-- extreme values: very sharp logits and all-zero queries.
+- extreme values: very sharp logits and all-zero queries;
+- the compute-unit count the plan's split rule reads is the device's own.
 """
 
 import numpy as np
@@ -158,3 +159,8 @@ def test_extreme_values(name, pow2):
         assert rel.max() <= 1.0
     if pow2 is None:
         np.testing.assert_array_equal(res["ranked"], np.tile(np.arange(res["nb"]), (wl.num_heads * res["nb"], 1)))
+
+
+def test_compute_units_is_the_device_count():
+    """The plan's split rule uses this count; it is the device's own."""
+    assert F.compute_units() == torch.cuda.get_device_properties(0).multi_processor_count
