@@ -75,17 +75,19 @@ __device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int bas
     constexpr int JJ = J0 >> decltype(sl)::value;
     if constexpr (JJ == 64) {
       const bool asc = ((base + lane) & kk) == 0;
-      const uint32_t lo = v[0] < v[1] ? v[0] : v[1], hi = v[0] < v[1] ? v[1] : v[0];
-      v[0] = asc ? lo : hi;
-      v[1] = asc ? hi : lo;
+      const uint32_t x = v[0], y = v[1];
+      const bool keep = (x < y) == asc;  // the pair is already in this chunk's order
+      v[0] = keep ? x : y;
+      v[1] = keep ? y : x;
     } else {
       const bool lower = (lane & JJ) == 0;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const bool asc = ((base + 64 * e + lane) & kk) == 0;
         const uint32_t a = v[e], b = xor_lane<JJ>(a);
-        const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
-        v[e] = (lower == asc) ? lo : hi;
+        // the lower side of an ascending pair keeps the smaller key: one
+        // compare picks between a and b
+        v[e] = ((a < b) == (lower == asc)) ? a : b;
       }
     }
   });

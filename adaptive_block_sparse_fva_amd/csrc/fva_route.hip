@@ -278,8 +278,9 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
         for (int e = 0; e < E; ++e) {
           const bool desc = ((e * 64 + lane) & KK) == 0;
           const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          key[e] = (lower == desc) ? hi : lo;
+          // the slot keeps the larger key where its side and direction agree,
+          // else the smaller: one compare picks between a and b
+          key[e] = ((a > b) == (lower == desc)) ? a : b;
         }
       }
     });
@@ -397,8 +398,7 @@ __device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, in
         for (int e = 0; e < EL; ++e) {
           const bool desc = ((x0 + e * 64) & KK) == 0;
           const uint64_t a = key[e], b = xbuf[((v ^ WJ) * EL + e) * 64 + lane];
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          key[e] = (lower == desc) ? hi : lo;
+          key[e] = ((a > b) == (lower == desc)) ? a : b;
         }
         __syncthreads();
       } else if constexpr (JJ >= 64) {
@@ -420,8 +420,9 @@ __device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, in
         for (int e = 0; e < EL; ++e) {
           const bool desc = ((x0 + e * 64) & KK) == 0;
           const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          key[e] = (lower == desc) ? hi : lo;
+          // the slot keeps the larger key where its side and direction agree,
+          // else the smaller: one compare picks between a and b
+          key[e] = ((a > b) == (lower == desc)) ? a : b;
         }
       }
     });
