@@ -18,15 +18,17 @@ from .fva import (  # noqa: F401
     block_importance,
     gsrs_action,
     gsrs_schedule,
+    kv_layout,
     load_library,
     make_problem,
     mfma_probe,
     plan,
     reselect,
     route,
+    schedule,
     sasa_refill,
     sizes,
     sparse_attn_fwd,
 )
 
-__version__ = "0.3.0"
+__version__ = "0.4.0"

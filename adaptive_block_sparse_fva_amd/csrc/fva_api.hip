@@ -17,11 +17,16 @@ int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked
                 const int32_t* row_count, const int32_t* head_refill, int32_t* row_ptr, int32_t* col_idx,
                 int32_t* head_count_final, int32_t* work_order, int32_t* plan_meta,
                 uint32_t* tile_counter, hipStream_t stream);
+int launch_kv_layout(const fva_problem& p, int nb, const void* k, const void* v, int32_t* order,
+                     void* kv, hipStream_t stream);
+int launch_schedule(const fva_problem& p, int nb, int split_s, const int32_t* row_ptr,
+                    int32_t* work_order, int32_t* plan_meta, uint32_t* tile_counter,
+                    hipStream_t stream);
 int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const void* kv,
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                 const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
                 void* o, float* lse, float* block_lse, void* workspace, float sm_scale,
-                hipStream_t stream);
+                int64_t* item_trace, hipStream_t stream);
 int launch_block_importance(const fva_problem& p, int nb, const int32_t* order, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* lse, const float* block_lse,
                             float* importance, hipStream_t stream);
@@ -120,8 +125,13 @@ static int check_problem(const fva_problem* p, int* nb_out) {
   return FVA_OK;
 }
 
-static int64_t workspace_need(const fva_problem* p, int nb) {
+// Routing workspace: the pooled block means (2 x H x nb x d floats), then
+// room for the scores (H x nb x nb floats) for callers that do not want them.
+static int64_t pooled_bytes(const fva_problem* p, int nb) {
   return 2 * (int64_t)p->num_heads * nb * p->head_dim * (int64_t)sizeof(float);
+}
+static int64_t workspace_need(const fva_problem* p, int nb) {
+  return pooled_bytes(p, nb) + (int64_t)p->num_heads * nb * nb * (int64_t)sizeof(float);
 }
 
 // K and V of every head re-laid out in position order: 2 x H x nb*B x d bf16.
@@ -141,6 +151,14 @@ static int64_t attn_workspace_need(const fva_problem* p, int nb) {
   return max_splits(p, nb) * 2 * ((int64_t)p->block * p->head_dim + 2 * p->block) * 4;
 }
 
+// The split rule's S: a tile is cut when it is heavier than about the mean
+// load of one compute unit (the two workgroups a unit runs share its
+// throughput, so anything lighter is absorbed by the heaviest-first queue).
+static int split_rule(int cus) {
+  const int split_s = cus / 2 < FVA_MAX_SPLITS / 2 ? cus / 2 : FVA_MAX_SPLITS / 2;
+  return split_s < 1 ? 1 : split_s;
+}
+
 static float effective_scale(const fva_problem* p) {
   return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
 }
@@ -151,7 +169,7 @@ using namespace fva;
 
 extern "C" {
 
-int fva_version(void) { return 300; }
+int fva_version(void) { return 400; }
 
 const char* fva_status_string(int status) {
   switch (status) {
@@ -214,16 +232,26 @@ int fva_route(const fva_problem* prob, const void* q, const void* k, const void*
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
-  if (!q || !k || !v || !scores || !ranked || !row_count || !head_count || !order || !kv ||
-      !workspace)
-    return FVA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kv) || !aligned16(workspace))
-    return FVA_ERR_ARG;
+  if (!q || !k || !ranked || !row_count || !head_count || !order || !workspace) return FVA_ERR_ARG;
+  if ((v == nullptr) != (kv == nullptr)) return FVA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(workspace)) return FVA_ERR_ARG;
+  if (kv && (!aligned16(v) || !aligned16(kv))) return FVA_ERR_ARG;
   if ((int64_t)workspace_bytes < workspace_need(prob, nb)) return FVA_ERR_WORKSPACE;
   float* qbar = (float*)workspace;
   float* kbar = qbar + (int64_t)prob->num_heads * nb * prob->head_dim;
+  if (scores == nullptr) scores = (float*)((char*)workspace + pooled_bytes(prob, nb));
   return launch_route(*prob, nb, q, k, v, scores, ranked, row_count, head_count, order, kv, qbar,
                       kbar, effective_scale(prob), (hipStream_t)stream);
+}
+
+int fva_kv_layout(const fva_problem* prob, const void* k, const void* v, int32_t* order, void* kv,
+                  void* stream) {
+  int nb = 0;
+  const int st = check_problem(prob, &nb);
+  if (st) return st;
+  if (!k || !v || !order || !kv) return FVA_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kv)) return FVA_ERR_ARG;
+  return launch_kv_layout(*prob, nb, k, v, order, kv, (hipStream_t)stream);
 }
 
 int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_count,
@@ -237,20 +265,27 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked, const int32_t* row_
     return FVA_ERR_ARG;
   const int cus = device_cu_count();
   if (cus < 1) return record_hip_error(hipErrorNoDevice, "compute unit count");
-  // a tile is cut when it is heavier than about the mean load of one compute
-  // unit: the two workgroups a unit runs share its throughput, so anything
-  // lighter is absorbed by the heaviest-first queue
-  int split_s = cus / 2 < FVA_MAX_SPLITS / 2 ? cus / 2 : FVA_MAX_SPLITS / 2;
-  if (split_s < 1) split_s = 1;
-  return launch_plan(*prob, nb, split_s, ranked, row_count, head_refill, row_ptr, col_idx,
+  return launch_plan(*prob, nb, split_rule(cus), ranked, row_count, head_refill, row_ptr, col_idx,
                      head_count_final, work_order, plan_meta, tile_counter, (hipStream_t)stream);
 }
 
-int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
-                        const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
-                        const int32_t* work_order, const int32_t* plan_meta,
-                        uint32_t* tile_counter, void* o, float* lse, float* block_lse,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+int fva_schedule(const fva_problem* prob, const int32_t* row_ptr, int32_t* work_order,
+                 int32_t* plan_meta, uint32_t* tile_counter, void* stream) {
+  int nb = 0;
+  const int st = check_problem(prob, &nb);
+  if (st) return st;
+  if (!row_ptr || !work_order || !plan_meta || !tile_counter) return FVA_ERR_ARG;
+  const int cus = device_cu_count();
+  if (cus < 1) return record_hip_error(hipErrorNoDevice, "compute unit count");
+  return launch_schedule(*prob, nb, split_rule(cus), row_ptr, work_order, plan_meta, tile_counter,
+                         (hipStream_t)stream);
+}
+
+static int attn_call(const fva_problem* prob, const void* q, const void* kv,
+                     const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
+                     const int32_t* work_order, const int32_t* plan_meta,
+                     uint32_t* tile_counter, void* o, float* lse, float* block_lse,
+                     void* workspace, size_t workspace_bytes, int64_t* item_trace, void* stream) {
   int nb = 0;
   int st = check_problem(prob, &nb);
   if (st) return st;
@@ -266,8 +301,28 @@ int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
   st = attn_grid(*prob, nb, &grid);
   if (st) return st;
   return launch_attn(*prob, nb, grid, q, kv, order, row_ptr, col_idx, work_order, plan_meta,
-                     tile_counter, o, lse, block_lse, workspace, effective_scale(prob),
+                     tile_counter, o, lse, block_lse, workspace, effective_scale(prob), item_trace,
                      (hipStream_t)stream);
+}
+
+int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
+                        const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
+                        const int32_t* work_order, const int32_t* plan_meta,
+                        uint32_t* tile_counter, void* o, float* lse, float* block_lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_call(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta, tile_counter, o, lse,
+                   block_lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int fva_sparse_attn_fwd_traced(const fva_problem* prob, const void* q, const void* kv,
+                               const int32_t* order, const int32_t* row_ptr,
+                               const int32_t* col_idx, const int32_t* work_order,
+                               const int32_t* plan_meta, uint32_t* tile_counter, void* o,
+                               float* lse, float* block_lse, void* workspace,
+                               size_t workspace_bytes, int64_t* item_trace, void* stream) {
+  if (item_trace == nullptr || ((uintptr_t)item_trace & 7u) != 0) return FVA_ERR_ARG;
+  return attn_call(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta, tile_counter, o, lse,
+                   block_lse, workspace, workspace_bytes, item_trace, stream);
 }
 
 int fva_block_importance(const fva_problem* prob, const int32_t* order, const int32_t* row_ptr,

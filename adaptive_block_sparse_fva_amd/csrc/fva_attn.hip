@@ -15,11 +15,10 @@
 //     B = Q fragments kept in registers for the whole tile, so every lane owns
 //     one query column and the softmax row statistics stay in-lane (one
 //     cross-half shuffle for the maximum per block);
-//   - O^T += V^T P^T: A = V^T fragments read from row-major V in LDS with the
-//     transposing LDS load (ds_read_b64_tr_b16), B = P converted to bf16
-//     straight from the S^T accumulators; the key permutation implied by the
-//     accumulator layout is applied to the V^T reads, so no register shuffles
-//     are needed;
+//   - O^T += V^T P^T: A = V^T fragments, one 16-byte LDS load each from a
+//     V^T sub-tile whose columns are already in the order the S^T
+//     accumulators hold their keys; B = P converted to bf16 straight from
+//     the S^T accumulators, so no register shuffles are needed;
 //   - K and V come re-laid out in the video-aware order by the routing pass
 //     (K row-major per position, V transposed per 64-position sub-block with
 //     its columns in the order the S^T accumulators hold their keys), so the
@@ -58,6 +57,7 @@ struct AttnArgs {
   int n, nb, num_tiles;
   int npad;          // nb * B
   float scale_log2;  // sm_scale * log2(e)
+  int64_t* item_trace;        // traced launches only: FVA_TRACE_FIELDS per work item
 };
 
 // Buffer resource over one head's rows of the re-laid-out K or V: raw byte
@@ -103,12 +103,21 @@ __device__ __forceinline__ int swz(int r) {
   else return (r >> 1) & 7;
 }
 
+// Placement of the calling wave: XCC id (hardware register 20 on this
+// family) in bits 32.., the hardware id register (wave, SIMD, CU, shader
+// array and engine fields) below.
+__device__ __forceinline__ int64_t wave_placement() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20);
+  return ((int64_t)xcc << 32) | hw;
+}
+
 // One workgroup = one (head, query block) tile at a time; KB = keys per
 // sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks,
 // numbered u = 0 .. nsub-1 along the tile's kept list).  K and V^T sub-tiles
 // stream through a ring of NBUF LDS slots: sub-block u+NBUF-1 is issued while
 // u is computed.
-template <int D, int BLK, int KB, int NBUF>
+template <int D, int BLK, int KB, int NBUF, bool TRACE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = BLK / 32;   // waves per workgroup (32 query rows each)
@@ -190,6 +199,11 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   int idx = blockIdx.x;
   while (idx < num_items) {
 
+    int64_t rt0 = 0, clk0 = 0;
+    if constexpr (TRACE) {
+      rt0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+      clk0 = (int64_t)__builtin_amdgcn_s_memtime();
+    }
     // work item: a whole tile, or one part of a split tile's kept list
     const int item = a.work_order[idx];
     const int t = item >> 1;
@@ -432,6 +446,19 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       if (hf == 0 && a.lse != nullptr)
         a.lse[(int64_t)h * a.n + qtok] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     }
+    if constexpr (TRACE) {
+      if (tid == 0) {
+        const int64_t clk1 = (int64_t)__builtin_amdgcn_s_memtime();
+        const int64_t rt1 = (int64_t)__builtin_amdgcn_s_memrealtime();
+        int64_t* tr = a.item_trace + (int64_t)idx * FVA_TRACE_FIELDS;
+        tr[0] = rt0;
+        tr[1] = rt1;
+        tr[2] = clk0;
+        tr[3] = clk1;
+        tr[4] = wave_placement();
+        tr[5] = blockIdx.x;
+      }
+    }
     if (tid == 0) s_tile = (int)gridDim.x + (int)atomicAdd(&a.tile_counter[0], 1u);
     __syncthreads();  // every wave is past its last use of s_cols; s_tile is set
     idx = s_tile;
@@ -444,7 +471,10 @@ constexpr int RING_SLOTS = FVA_NBUF;
 
 template <int D, int BLK>
 static int launch_attn_t(const AttnArgs& args, int grid, hipStream_t stream) {
-  sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS><<<grid, BLK * 2, 0, stream>>>(args);
+  if (args.item_trace)
+    sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS, true><<<grid, BLK * 2, 0, stream>>>(args);
+  else
+    sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS, false><<<grid, BLK * 2, 0, stream>>>(args);
   return record_hip_error(hipGetLastError(), "sparse_attn_fwd launch");
 }
 
@@ -517,8 +547,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 
 template <int D, int BLK>
 static int occupancy_t(int* blocks) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS>,
-                                                           BLK * 2, 0);
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks, sparse_attn_fwd_kernel<D, BLK, KEYS_PER_STEP, RING_SLOTS, false>, BLK * 2, 0);
 }
 
 // Resident workgroups per CU for the (d, B) instantiation, or -1 on error.
@@ -551,7 +581,7 @@ int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const voi
                 const int32_t* order, const int32_t* row_ptr, const int32_t* col_idx,
                 const int32_t* work_order, const int32_t* plan_meta, uint32_t* tile_counter,
                 void* o, float* lse, float* block_lse, void* workspace, float sm_scale,
-                hipStream_t stream) {
+                int64_t* item_trace, hipStream_t stream) {
   const int npad = nb * p.block;
   const bf16_t* kp = (const bf16_t*)kv;
   const bf16_t* vt = kp + (int64_t)p.num_heads * npad * p.head_dim;
@@ -570,6 +600,7 @@ int launch_attn(const fva_problem& p, int nb, int grid, const void* q, const voi
   a.plan_meta = plan_meta;
   a.tile_counter = tile_counter;
   a.partial = (float*)workspace;
+  a.item_trace = item_trace;
   a.stride_head = p.stride_head;
   a.stride_token = p.stride_token;
   a.n = p.seq_len;

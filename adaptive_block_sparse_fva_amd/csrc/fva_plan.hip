@@ -104,6 +104,11 @@ __device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int bas
 // larger than a unit's mean load.  Split tiles get slots 0, 1, ... in tile-id
 // order.  Fewer than 2 * split_s tiles can qualify, and
 // split_s <= FVA_MAX_SPLITS / 2.
+//
+// FROM_CSR: the row lengths come from a given row_ptr (fva_schedule) instead
+// of the refill of row_count; row_ptr and head_count_final are then inputs /
+// unused and only the work list, plan_meta and the counter are written.
+template <bool FROM_CSR>
 __device__ __forceinline__ void plan_scan(
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ head_refill, int rows, int nb,
     int refill_per_mille, int split_s,
@@ -138,7 +143,8 @@ __device__ __forceinline__ void plan_scan(
   };
 
   auto kept = [&](int r) {
-    return refill_count(row_count[r], nb, row_refill(head_refill, r, nb, refill_per_mille));
+    if constexpr (FROM_CSR) return row_ptr[r + 1] - row_ptr[r];
+    else return refill_count(row_count[r], nb, row_refill(head_refill, r, nb, refill_per_mille));
   };
 
   // per-thread contiguous chunk of rows
@@ -151,11 +157,13 @@ __device__ __forceinline__ void plan_scan(
 
   // row offsets, then per-head totals from them (the stores are complete and
   // visible to the workgroup after the barrier inside the next scan)
-  for (int r = r0; r < r1; ++r) {
-    row_ptr[r] = run;
-    run += kept(r);
+  if constexpr (!FROM_CSR) {
+    for (int r = r0; r < r1; ++r) {
+      row_ptr[r] = run;
+      run += kept(r);
+    }
+    if (r1 == rows && r0 < r1) row_ptr[rows] = run;
   }
-  if (r1 == rows && r0 < r1) row_ptr[rows] = run;
 
   // split decision and slots
   const int mean = (total + split_s - 1) / split_s;
@@ -164,8 +172,9 @@ __device__ __forceinline__ void plan_scan(
   for (int r = r0; r < r1; ++r) nsp += is_split(kept(r)) ? 1 : 0;
   int nsplit = 0;
   int sp = block_scan(nsp, &nsplit);
-  for (int hh = tid; hh < rows / nb; hh += PLAN_THREADS)
-    head_count_final[hh] = row_ptr[(hh + 1) * nb] - row_ptr[hh * nb];
+  if constexpr (!FROM_CSR)
+    for (int hh = tid; hh < rows / nb; hh += PLAN_THREADS)
+      head_count_final[hh] = row_ptr[(hh + 1) * nb] - row_ptr[hh * nb];
 
   // work items: tile r's items start at r + (split tiles before r)
   for (int r = r0; r < r1; ++r) {
@@ -306,8 +315,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ head_count_final,
     int32_t* __restrict__ work_order, int32_t* __restrict__ plan_meta, uint32_t* __restrict__ tile_counter) {
   if (blockIdx.x == 0) {
-    plan_scan(row_count, head_refill, rows, nb, refill_per_mille, split_s, row_ptr, head_count_final, work_order,
-              plan_meta, tile_counter);
+    plan_scan<false>(row_count, head_refill, rows, nb, refill_per_mille, split_s, row_ptr, head_count_final,
+                     work_order, plan_meta, tile_counter);
   } else {
     // fill workgroup f of F takes the rows [f * per, (f + 1) * per), per a
     // multiple of four
@@ -318,17 +327,38 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   }
 }
 
+// The placement step alone, from a given CSR mask (fva_schedule).
+__global__ __launch_bounds__(PLAN_THREADS) void schedule_kernel(
+    const int32_t* __restrict__ row_ptr, int rows, int nb, int split_s, int32_t* __restrict__ work_order,
+    int32_t* __restrict__ plan_meta, uint32_t* __restrict__ tile_counter) {
+  plan_scan<true>(nullptr, nullptr, rows, nb, 0, split_s, const_cast<int32_t*>(row_ptr), nullptr, work_order,
+                  plan_meta, tile_counter);
+}
+
+// LDS of the work-list sort: the item count padded to a power of two (>= 128).
+static size_t sort_lds_bytes(int rows) {
+  const int cap = rows + (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS);
+  int ipad = 128;
+  while (ipad < cap) ipad <<= 1;
+  return (size_t)ipad * sizeof(uint32_t);
+}
+
+int launch_schedule(const fva_problem& p, int nb, int split_s, const int32_t* row_ptr,
+                    int32_t* work_order, int32_t* plan_meta, uint32_t* tile_counter,
+                    hipStream_t stream) {
+  const int rows = p.num_heads * nb;
+  schedule_kernel<<<1, PLAN_THREADS, sort_lds_bytes(rows), stream>>>(row_ptr, rows, nb, split_s, work_order,
+                                                                      plan_meta, tile_counter);
+  return record_hip_error(hipGetLastError(), "schedule launch");
+}
+
 int launch_plan(const fva_problem& p, int nb, int split_s, const int16_t* ranked,
                 const int32_t* row_count, const int32_t* head_refill, int32_t* row_ptr,
                 int32_t* col_idx, int32_t* head_count_final, int32_t* work_order,
                 int32_t* plan_meta, uint32_t* tile_counter, hipStream_t stream) {
   const int rows = p.num_heads * nb;
-  // the sort's LDS: the item count padded to a power of two (>= 128)
-  const int cap = rows + (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS);
-  int ipad = 128;
-  while (ipad < cap) ipad <<= 1;
   const int fill_wgs = (rows + 3) / 4 < FILL_WGS_MAX ? (rows + 3) / 4 : FILL_WGS_MAX;
-  plan_kernel<<<1 + fill_wgs, PLAN_THREADS, ipad * sizeof(uint32_t), stream>>>(ranked, row_count, head_refill, rows, nb,
+  plan_kernel<<<1 + fill_wgs, PLAN_THREADS, sort_lds_bytes(rows), stream>>>(ranked, row_count, head_refill, rows, nb,
                                                                p.refill_per_mille, split_s, row_ptr, col_idx,
                                                                head_count_final, work_order, plan_meta, tile_counter);
   return record_hip_error(hipGetLastError(), "plan launch");

@@ -34,23 +34,20 @@ struct VRelayout {
   int block, nb, n;
 };
 
-// V of block b of head h, transposed per 64-position sub-block: a thread
-// gathers the 16-byte chunk dc (features 8dc .. 8dc+7) of the 8 keys that
-// make up output chunk jc (columns 8jc .. 8jc+7), transposes the 8 x 8 bf16
-// block in registers and writes 8 rows of 16 bytes.  The 8 keys of chunk jc
-// are vt_key(8jc + e) = 16(jc/2) + 4(jc%2) + 8(e/4) + e%4.  256 threads; tok
-// is 128 ints of LDS.
+// V of one block, transposed per 64-position sub-block: a thread gathers the
+// 16-byte chunk dc (features 8dc .. 8dc+7) of the 8 keys that make up output
+// chunk jc (columns 8jc .. 8jc+7), transposes the 8 x 8 bf16 block in
+// registers and writes 8 rows of 16 bytes.  The 8 keys of chunk jc are
+// vt_key(8jc + e) = 16(jc/2) + 4(jc%2) + 8(e/4) + e%4.  256 threads; tok
+// holds the block's tokens in LDS (rb real ones), x points at the head's V,
+// dst_blk at the block's first V^T sub-tile.
 template <int D>
-__device__ __forceinline__ void vt_relayout_block(const VRelayout& r, int b, int h, int32_t* tok) {
+__device__ __forceinline__ void vt_transpose_block(const bf16_t* __restrict__ x, int64_t stride_token,
+                                                   const int32_t* tok, int rb, int block,
+                                                   bf16_t* __restrict__ dst_blk) {
   const int tid = threadIdx.x;
-  const int block = r.block;
-  if (tid < block) tok[tid] = r.order[b * block + tid];
-  __syncthreads();
-  const int rb = min(block, r.n - b * block);
-  const int64_t npad = (int64_t)r.nb * block;
   constexpr int DCH = D / 8;
   constexpr int PER_SB = (VT_KEYS / 8) * DCH;
-  const bf16_t* x = r.v + (int64_t)h * r.stride_head;
   for (int w = tid; w < (block / VT_KEYS) * PER_SB; w += 256) {
     const int sb = w / PER_SB, rem = w % PER_SB;
     const int jc = rem / DCH, dc = rem % DCH;
@@ -60,9 +57,9 @@ __device__ __forceinline__ void vt_relayout_block(const VRelayout& r, int b, int
     for (int e = 0; e < 8; ++e) {
       const int key = k0 + 8 * (e >> 2) + (e & 3);
       in[e] = u32x4{0u, 0u, 0u, 0u};
-      if (key < rb) in[e] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[key] * r.stride_token + dc * 8);
+      if (key < rb) in[e] = *reinterpret_cast<const u32x4*>(x + (int64_t)tok[key] * stride_token + dc * 8);
     }
-    bf16_t* dst = r.vt + ((int64_t)h * npad + (int64_t)b * block + sb * VT_KEYS) * D + (8 * dc) * VT_KEYS + jc * 8;
+    bf16_t* dst = dst_blk + (int64_t)(sb * VT_KEYS) * D + (8 * dc) * VT_KEYS + jc * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // feature 8dc + i of keys e = 0..7: the low (i even) or high (i odd)
@@ -75,6 +72,61 @@ __device__ __forceinline__ void vt_relayout_block(const VRelayout& r, int b, int
       *reinterpret_cast<u32x4*>(dst + i * VT_KEYS) = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
+}
+
+// V re-layout of block b of head h inside the select launch (the order
+// table has been written by the pooling launch).  tok is 128 ints of LDS.
+template <int D>
+__device__ __forceinline__ void vt_relayout_block(const VRelayout& r, int b, int h, int32_t* tok) {
+  const int tid = threadIdx.x;
+  const int block = r.block;
+  if (tid < block) tok[tid] = r.order[b * block + tid];
+  __syncthreads();
+  const int rb = min(block, r.n - b * block);
+  const int64_t npad = (int64_t)r.nb * block;
+  vt_transpose_block<D>(r.v + (int64_t)h * r.stride_head, r.stride_token, tok, rb, block,
+                        r.vt + ((int64_t)h * npad + (int64_t)b * block) * D);
+}
+
+// K and V of block b of head h in the attention's layout, from the caller's
+// tensors alone (fva_kv_layout): the block's tokens from the closed-form
+// order, K rows copied in position order (zero rows past the end, all loads
+// in flight before the stores), V transposed as above.  Workgroups of head 0
+// also publish the order table.
+template <int D>
+__global__ __launch_bounds__(256) void kv_layout_kernel(
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int64_t stride_head,
+    int64_t stride_token, OrderGeo geo, int block, int nb, int32_t* __restrict__ order,
+    bf16_t* __restrict__ kp, bf16_t* __restrict__ vt) {
+  constexpr int CH = D / 8;
+  constexpr int MAXIT = 128 * CH / 256;
+  __shared__ int32_t tok[128];
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int rb = min(block, geo.n - b * block);
+  if (tid < block) {
+    const int t = geo.token(b * block + tid);
+    tok[tid] = t;
+    if (h == 0) order[b * block + tid] = t;
+  }
+  __syncthreads();
+  const int64_t npad = (int64_t)nb * block;
+  const bf16_t* xk = k + (int64_t)h * stride_head;
+  u32x4 rows[MAXIT];
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int x = tid + it * 256, r = x / CH, c = x % CH;
+    rows[it] = u32x4{0u, 0u, 0u, 0u};
+    if (r < rb) rows[it] = *reinterpret_cast<const u32x4*>(xk + (int64_t)tok[r] * stride_token + c * 8);
+  }
+  bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int x = tid + it * 256, r = x / CH, c = x % CH;
+    if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = rows[it];
+  }
+  vt_transpose_block<D>(v + (int64_t)h * stride_head, stride_token, tok, rb, block,
+                        vt + ((int64_t)h * npad + (int64_t)b * block) * D);
 }
 // (at least 5 workgroups per compute unit, so that a 5-head problem's
 // workgroups are all resident at once)
@@ -120,12 +172,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
       krows[it] = *reinterpret_cast<const u32x4*>(xk + off);
     }
   }
-  // K rows in position order, zero rows past the end
-  bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
+  // K rows in position order, zero rows past the end (when the caller asked
+  // for the attention's K/V layout)
+  if (kp != nullptr) {
+    bf16_t* dst = kp + ((int64_t)h * npad + (int64_t)b * block) * D;
 #pragma unroll
-  for (int it = 0; it < MAXIT; ++it) {
-    const int r = rg + it * RG;
-    if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = krows[it];
+    for (int it = 0; it < MAXIT; ++it) {
+      const int r = rg + it * RG;
+      if (r < block) *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + c * 8) = krows[it];
+    }
   }
   auto column_sums = [&](const u32x4(&rows)[MAXIT], float(&pt)[RG][D]) {
     float acc[8];
@@ -701,8 +756,9 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
                  float sm_scale, hipStream_t stream) {
   const OrderGeo geo = make_order_geo(p);
   const dim3 pool_grid(nb, p.num_heads);
+  // kv == nullptr: routing only (Q and K read, nothing re-laid out)
   bf16_t* kp = (bf16_t*)kv;
-  bf16_t* vt = kp + (int64_t)p.num_heads * nb * p.block * p.head_dim;
+  bf16_t* vt = kp ? kp + (int64_t)p.num_heads * nb * p.block * p.head_dim : nullptr;
   if (p.head_dim == 128)
     route_pool_kernel<128><<<pool_grid, 256, 0, stream>>>(
         (const bf16_t*)q, (const bf16_t*)k, p.stride_head, p.stride_token, geo, p.block, nb,
@@ -722,8 +778,8 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   st = record_hip_error(hipGetLastError(), "route_scores launch");
   if (st) return st;
 
-  // the select launch also carries the V re-layout, one workgroup per
-  // (head, block); a share of it in the scores launch was slower (those
+  // with kv, the select launch also carries the V re-layout, one workgroup
+  // per (head, block); a share of it in the scores launch was slower (those
   // workgroups would hold the score tiles' 66 KB of LDS each)
   const int rows = p.num_heads * nb;
   const VRelayout vr{(const bf16_t*)v, p.stride_head, p.stride_token, order, vt, p.block, nb, p.seq_len};
@@ -732,7 +788,7 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   // ranking workgroups: four rows each (one wave per row), or two rows each
   // (two waves per row) when a row has more than 256 blocks (E >= 8)
   const int sel_wgs = e >= 8 ? (rows + 1) / 2 : (rows + 4 * SEL_ROWS - 1) / (4 * SEL_ROWS);
-  const int grid = sel_wgs + rows;
+  const int grid = sel_wgs + (kv ? rows : 0);
 #define FVA_SELECT(E_)                                                                               \
   do {                                                                                               \
     if (p.head_dim == 128)                                                                           \
@@ -752,6 +808,21 @@ int launch_route(const fva_problem& p, int nb, const void* q, const void* k, con
   }
 #undef FVA_SELECT
   return record_hip_error(hipGetLastError(), "route_select launch");
+}
+
+int launch_kv_layout(const fva_problem& p, int nb, const void* k, const void* v, int32_t* order,
+                     void* kv, hipStream_t stream) {
+  const OrderGeo geo = make_order_geo(p);
+  const dim3 grid(nb, p.num_heads);
+  bf16_t* kp = (bf16_t*)kv;
+  bf16_t* vt = kp + (int64_t)p.num_heads * nb * p.block * p.head_dim;
+  if (p.head_dim == 128)
+    kv_layout_kernel<128><<<grid, 256, 0, stream>>>((const bf16_t*)k, (const bf16_t*)v, p.stride_head,
+                                                    p.stride_token, geo, p.block, nb, order, kp, vt);
+  else
+    kv_layout_kernel<64><<<grid, 256, 0, stream>>>((const bf16_t*)k, (const bf16_t*)v, p.stride_head,
+                                                   p.stride_token, geo, p.block, nb, order, kp, vt);
+  return record_hip_error(hipGetLastError(), "kv_layout launch");
 }
 
 }  // namespace fva

@@ -45,14 +45,18 @@ FVA_GSRS_DENSE = 0
 FVA_GSRS_FULL_SEARCH = 1
 FVA_GSRS_CANDIDATE_SEARCH = 2
 FVA_GSRS_REUSE = 3
+FVA_TRACE_FIELDS = 6
 
 EXPORTED = (
     "fva_sizes",
     "fva_attn_workgroups",
     "fva_compute_units",
     "fva_route",
+    "fva_kv_layout",
     "fva_plan",
+    "fva_schedule",
     "fva_sparse_attn_fwd",
+    "fva_sparse_attn_fwd_traced",
     "fva_block_importance",
     "fva_mfma_probe",
     "fva_balance",
@@ -166,9 +170,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.fva_compute_units.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fva_kv_layout.argtypes = [P, vp, vp, vp, vp, vp]
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fva_schedule.argtypes = [P, vp, vp, vp, vp, vp]
     lib.fva_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+    lib.fva_sparse_attn_fwd_traced.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_size_t, vp, vp]
     lib.fva_block_importance.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64,
                                    ctypes.POINTER(ctypes.c_double), vp]
@@ -183,9 +191,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_last_error.argtypes = []
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
-    for name in ("fva_sizes", "fva_attn_workgroups", "fva_compute_units", "fva_route", "fva_plan",
-                 "fva_sparse_attn_fwd", "fva_block_importance", "fva_mfma_probe", "fva_balance",
-                 "fva_sasa_refill", "fva_reselect", "fva_gsrs_action", "fva_version"):
+    for name in ("fva_sizes", "fva_attn_workgroups", "fva_compute_units", "fva_route",
+                 "fva_kv_layout", "fva_plan", "fva_schedule", "fva_sparse_attn_fwd",
+                 "fva_sparse_attn_fwd_traced", "fva_block_importance", "fva_mfma_probe",
+                 "fva_balance", "fva_sasa_refill", "fva_reselect", "fva_gsrs_action", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -254,11 +263,26 @@ def _stream(stream) -> int:
 
 def route(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, workspace,
           stream=None):
+    """fva_route; v and kv may both be None (routing only), scores may be None."""
     st = load_library().fva_route(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(scores),
                                   _ptr(ranked), _ptr(row_count), _ptr(head_count), _ptr(order),
                                   _ptr(kv), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "fva_route")
+
+
+def kv_layout(prob, k, v, order, kv, stream=None):
+    """fva_kv_layout: the caller's K and V in the attention's layout (and the order table)."""
+    st = load_library().fva_kv_layout(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(order), _ptr(kv),
+                                      _stream(stream))
+    _check(st, "fva_kv_layout")
+
+
+def schedule(prob, row_ptr, work_order, plan_meta, tile_counter, stream=None):
+    """fva_schedule: the heaviest-first work list of a given CSR mask."""
+    st = load_library().fva_schedule(ctypes.byref(prob), _ptr(row_ptr), _ptr(work_order),
+                                     _ptr(plan_meta), _ptr(tile_counter), _stream(stream))
+    _check(st, "fva_schedule")
 
 
 def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, work_order, plan_meta,
@@ -272,14 +296,18 @@ def plan(prob, ranked, row_count, row_ptr, col_idx, head_count_final, work_order
 
 
 def sparse_attn_fwd(prob, q, kv, order, row_ptr, col_idx, work_order, plan_meta, tile_counter, o,
-                    workspace, lse=None, block_lse=None, stream=None):
-    st = load_library().fva_sparse_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(kv), _ptr(order),
-                                            _ptr(row_ptr), _ptr(col_idx), _ptr(work_order),
-                                            _ptr(plan_meta), _ptr(tile_counter), _ptr(o),
-                                            _ptr(lse), _ptr(block_lse), _ptr(workspace),
-                                            workspace.numel() * workspace.element_size(),
-                                            _stream(stream))
-    _check(st, "fva_sparse_attn_fwd")
+                    workspace, lse=None, block_lse=None, stream=None, item_trace=None):
+    """fva_sparse_attn_fwd, or fva_sparse_attn_fwd_traced when item_trace (device int64
+    [work items][FVA_TRACE_FIELDS]) is given."""
+    lib = load_library()
+    args = [ctypes.byref(prob), _ptr(q), _ptr(kv), _ptr(order), _ptr(row_ptr), _ptr(col_idx),
+            _ptr(work_order), _ptr(plan_meta), _ptr(tile_counter), _ptr(o), _ptr(lse),
+            _ptr(block_lse), _ptr(workspace), workspace.numel() * workspace.element_size()]
+    if item_trace is None:
+        _check(lib.fva_sparse_attn_fwd(*args, _stream(stream)), "fva_sparse_attn_fwd")
+    else:
+        _check(lib.fva_sparse_attn_fwd_traced(*args, _ptr(item_trace), _stream(stream)),
+               "fva_sparse_attn_fwd_traced")
 
 
 def block_importance(prob, order, row_ptr, col_idx, lse, block_lse, importance, stream=None):
@@ -432,27 +460,44 @@ class Buffers:
             tile_counter=torch.zeros(sz.tile_counter_elems, **i32),
             attn_workspace=torch.empty(max(16, sz.attn_workspace_bytes) // 4, dtype=torch.float32,
                                        device=device),
-            o=torch.empty((H, N, d), dtype=torch.bfloat16, device=device),
+            # o follows the problem's strides, as q does (the kernels write it so)
+            o=torch.empty_strided((H, N, d), (prob.stride_head, prob.stride_token, 1),
+                                  dtype=torch.bfloat16, device=device),
             lse=torch.empty((H, N), dtype=torch.float32, device=device),
         )
 
-    def route(self, q, k, v, stream=None):
-        route(self.prob, q, k, v, self.scores, self.ranked, self.row_count, self.head_count,
-              self.order, self.kv, self.workspace, stream)
+    def route(self, q, k, v=None, stream=None, with_scores=True):
+        """Routing; with v also the K/V re-layout into .kv (in the same pass).
+        with_scores=False leaves the scores inside the workspace."""
+        route(self.prob, q, k, v, self.scores if with_scores else None, self.ranked,
+              self.row_count, self.head_count, self.order, None if v is None else self.kv,
+              self.workspace, stream)
+
+    def kv_layout(self, k, v, stream=None):
+        """K and V into .kv (and the order table into .order) without routing."""
+        kv_layout(self.prob, k, v, self.order, self.kv, stream)
+
+    def schedule(self, stream=None):
+        """Work list of the mask currently in .row_ptr (e.g. one written by the caller)."""
+        schedule(self.prob, self.row_ptr, self.work_order, self.plan_meta, self.tile_counter,
+                 stream)
 
     def plan(self, stream=None, head_refill=None):
         plan(self.prob, self.ranked, self.row_count, self.row_ptr, self.col_idx,
              self.head_count_final, self.work_order, self.plan_meta, self.tile_counter, stream,
              head_refill)
 
-    def attn(self, q, work_order=None, with_lse=True, block_lse=None, stream=None):
-        """Attention over the K/V that the last route() call re-laid out, the
-        work items taken in the plan's order (or in work_order's); block_lse
-        (float, >= row_ptr[-1] * B elements) also records per-block LSEs."""
+    def attn(self, q, work_order=None, with_lse=True, block_lse=None, stream=None,
+             item_trace=None):
+        """Attention over the K/V in .kv (from route(q, k, v) or kv_layout()),
+        the work items taken in the plan's order (or in work_order's);
+        block_lse (float, >= row_ptr[-1] * B elements) also records per-block
+        LSEs; item_trace (int64 [items][FVA_TRACE_FIELDS]) records per-item
+        clocks."""
         sparse_attn_fwd(self.prob, q, self.kv, self.order, self.row_ptr, self.col_idx,
                         self.work_order if work_order is None else work_order, self.plan_meta,
                         self.tile_counter, self.o, self.attn_workspace,
-                        self.lse if with_lse else None, block_lse, stream)
+                        self.lse if with_lse else None, block_lse, stream, item_trace)
 
     def importance(self, block_lse, out=None, stream=None):
         """Precise block importance [H][nb][nb] from the last attn(block_lse=...)."""

@@ -6,9 +6,12 @@ key block, later searches over the first search's mask only (the candidate
 set), the latest mask reused between searches, a lower Top-p at each search.
 
 This module only sequences library calls and keeps device buffers between
-steps: fva_gsrs_action decides what a step does; fva_route (order, K/V
-re-layout), fva_plan, fva_sparse_attn_fwd (with per-block LSEs at a search),
-fva_block_importance and fva_reselect do the work on the GPU.
+steps: fva_gsrs_action decides what a step does; fva_kv_layout (order, K/V
+re-layout of the step's inputs), fva_schedule (work list of the all-blocks
+mask), fva_plan, fva_sparse_attn_fwd (with per-block LSEs at a search),
+fva_block_importance and fva_reselect do the work on the GPU.  No step runs
+the pooled-score routing: every mask here comes from the precise importance
+of a search, or is the all-blocks mask.
 """
 
 from __future__ import annotations
@@ -20,7 +23,7 @@ import torch
 
 from .fva import (FVA_GSRS_CANDIDATE_SEARCH, FVA_GSRS_DENSE, FVA_GSRS_FULL_SEARCH,
                   FVA_GSRS_REUSE, Buffers, GsrsSchedule, Problem, block_importance,
-                  gsrs_action, plan, reselect, sizes, sparse_attn_fwd)
+                  gsrs_action, plan, reselect, schedule, sizes, sparse_attn_fwd)
 
 
 @dataclass
@@ -66,7 +69,12 @@ class GsrsRunner:
         self.full = MaskPlan.allocate(prob, device)
         self.candidates = MaskPlan.allocate(prob, device)
         self.current = MaskPlan.allocate(prob, device)
-        self.full_count = torch.full((sz.num_rows,), nb, dtype=torch.int32, device=device)
+        # the all-blocks mask: every row keeps 0 .. nb-1
+        rows = sz.num_rows
+        self.full.row_ptr.copy_(torch.arange(rows + 1, dtype=torch.int32, device=device) * nb)
+        self.full.col_idx[: rows * nb].copy_(
+            torch.arange(nb, dtype=torch.int32, device=device).repeat(rows))
+        self.full.head_count.fill_(nb * nb)
         self.sel_ranked = torch.empty(sz.ranked_elems, dtype=torch.int16, device=device)
         self.sel_count = torch.empty(sz.num_rows, dtype=torch.int32, device=device)
         self.sel_head = torch.empty(H, dtype=torch.int32, device=device)
@@ -87,10 +95,10 @@ class GsrsRunner:
 
     def step(self, t: int, q, k, v, stream=None):
         action, p = gsrs_action(self.schedule, t)
-        self.buf.route(q, k, v, stream)  # order and K/V re-layout for this step's inputs
+        self.buf.kv_layout(k, v, stream)  # order and K/V re-layout of this step's inputs
         if not self._have_full:
-            # every block of every row (the ranking only orders what is kept)
-            self._plan(self.buf.ranked, self.full_count, self.full, stream)
+            mp = self.full
+            schedule(self.prob, mp.row_ptr, mp.work_order, mp.plan_meta, mp.tile_counter, stream)
             self._have_full = True
         if action == FVA_GSRS_DENSE:
             self._attn(q, self.full, stream=stream)

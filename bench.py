@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--workload", default="rank480p")
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall-clock budget of the oracle's attention sample")
+                    help="wall-clock budget of the oracle's attention sample on workloads other "
+                         "than rank480p (rank480p runs every tile)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-balance", action="store_true",
@@ -87,9 +88,10 @@ def list_schedule_makespan(costs, workers):
     return max(heap)
 
 
-def cpu_baseline(wl, inp, p, gpu_o, row_ptr_gpu, col_idx_gpu, budget_s):
+def cpu_baseline(wl, inp, p, gpu_o, row_ptr_gpu, col_idx_gpu, budget_s, all_tiles):
     """The oracle as it stands, on the host cores: full routing + plan, and the
-    fp64 masked attention on a seeded sample of tiles bounded by budget_s."""
+    fp64 masked attention on every tile (all_tiles) or on a seeded sample of
+    tiles bounded by budget_s, extrapolated by kept FLOPs."""
     import numpy as np
     import oracle as O
     from synth import bf16_bits_to_f64
@@ -124,27 +126,67 @@ def cpu_baseline(wl, inp, p, gpu_o, row_ptr_gpu, col_idx_gpu, budget_s):
         done.append((err.max(), err.mean()))
         cols = col_idx_gpu[row_ptr_gpu[t]: row_ptr_gpu[t + 1]]
         flops += 4 * wl.head_dim * int(sizes[i]) * int(sizes[cols].sum())
-        if time.perf_counter() - start > budget_s:
+        if not all_tiles and time.perf_counter() - start > budget_s:
             break
     t_attn_sample = time.perf_counter() - start
     gpu_flops, _ = kept_flops_and_pairs(row_ptr_gpu, col_idx_gpu, wl.seq_len, wl.block,
                                         wl.head_dim, H, nb)
-    t_attn_full = t_attn_sample * gpu_flops / max(flops, 1)
+    complete = len(done) == H * nb
+    t_attn_full = t_attn_sample if complete else t_attn_sample * gpu_flops / max(flops, 1)
     value_ms = (t1 - t0 + t2 - t1 + t_attn_full) * 1e3
     errs = np.array(done)
+    if complete:
+        what = (f"fp64 masked attention on all {H * nb} tiles ({gpu_flops / 1e9:.1f} GFLOP kept, "
+                f"{t_attn_sample:.1f}s)")
+    else:
+        what = (f"fp64 masked attention on {len(done)} of {H * nb} seeded-random tiles "
+                f"({flops / 1e9:.1f} of {gpu_flops / 1e9:.1f} GFLOP kept, {t_attn_sample:.1f}s), "
+                f"extrapolated by kept FLOPs")
     return {
         "value": round(value_ms, 1),
         "unit": "ms",
         "cores": blas_threads if blas_threads else cores,
         "kind": "oracle",
-        "sample": (f"full routing+plan ({t1 - t0:.2f}s + {t2 - t1:.2f}s); fp64 masked attention on "
-                   f"{len(done)} of {H * nb} seeded-random tiles ({flops / 1e9:.1f} of "
-                   f"{gpu_flops / 1e9:.1f} GFLOP kept, {t_attn_sample:.1f}s), extrapolated by kept FLOPs"),
+        "sample": f"full routing+plan ({t1 - t0:.2f}s + {t2 - t1:.2f}s); {what}",
         "host_cores_visible": cores,
         "sample_parity": {"o_max_abs": float(errs[:, 0].max()), "o_mean_abs": float(errs[:, 1].mean()),
-                          "tiles": len(done)},
-        "oracle_matches_gpu_mask": bool(np.array_equal(pl["row_ptr"], row_ptr_gpu)),
+                          "o_mean_abs_per_tile_max": float(errs[:, 1].max()), "tiles": len(done)},
+        "oracle_matches_gpu_mask": bool(np.array_equal(pl["row_ptr"], row_ptr_gpu)
+                                        and np.array_equal(pl["col_idx"], col_idx_gpu)),
     }
+
+
+def measured_cu_imbalance(trace, grid):
+    """The one-GPU analog of FVAttn S2.2 Eq 2 from a traced attention launch:
+    per-item start/end clocks grouped by workgroup and by compute unit.
+
+    load = the summed durations of the items a unit (or workgroup) ran;
+    finish = when its last item ended, from the launch's first item start.
+    rho = max / mean of each, over the units that ran items."""
+    import numpy as np
+    rt0, rt1, c0, c1, place, wg = (trace[:, j] for j in range(6))
+    start = rt0.min()
+    xcc = (place >> 32) & 0xffff
+    cu = (xcc << 8) | ((place >> 8) & 0xff)  # XCC, engine, array and CU fields
+    dur = (rt1 - rt0).astype(np.float64)
+
+    def rho(keys):
+        uk, inv = np.unique(keys, return_inverse=True)
+        load = np.bincount(inv, weights=dur)
+        fin = np.zeros(len(uk))
+        np.maximum.at(fin, inv, (rt1 - start).astype(np.float64))
+        return len(uk), float(load.max() / load.mean()), float(fin.max() / fin.mean())
+
+    n_cu, rho_cu_load, rho_cu_finish = rho(cu)
+    n_wg, rho_wg_load, rho_wg_finish = rho(wg)
+    span_us = float(rt1.max() - start) / 100.0  # 100 MHz constant clock
+    return {"clock": "s_memrealtime (100 MHz) per work item, one traced launch",
+            "compute_units_seen": int(n_cu), "workgroups_seen": int(n_wg),
+            "per_compute_unit": {"load": round(rho_cu_load, 4), "finish": round(rho_cu_finish, 4)},
+            "per_workgroup": {"load": round(rho_wg_load, 4), "finish": round(rho_wg_finish, 4)},
+            "span_us": round(span_us, 1),
+            "mean_item_us": round(float(dur.mean()) / 100.0, 2),
+            "cycles_per_us": round(float((c1 - c0).sum()) / float(dur.sum()) * 100.0, 1)}
 
 
 def balance_simulation(stream, cpu_reps=200, reps=3):
@@ -449,24 +491,43 @@ def main():
     dense_flops = 4.0 * N * N * d * H
     attn_avg_ms = float(t_attn.mean())
     achieved_tflops = kept / (attn_avg_ms * 1e-3) / 1e12
-    # route reads Q, K, V once, writes K and V re-laid out, the scores, the
-    # ranking, the counts and the order table
-    route_bytes = (3 * H * N * d * 2 + 2 * H * nb * B * d * 2 + H * nb * nb * (4 + 2)
-                   + H * nb * 4 * 2 + nb * B * 4)
-    # the routing rate is taken over routing calls back to back (same inputs,
+    # Routing (FVAttn S3.1: pooled Q/K scores, Top-p + floor, counts,
+    # ranking) on its own algorithmic bytes: Q and K read once, the ranking,
+    # the counts and the order table written (the scores stay in the
+    # workspace).  The step itself runs the fused pass, which also writes K
+    # and V in the attention's layout (V read once more, K and V written) and
+    # exports the scores; that pass and the K/V re-layout on its own are
+    # reported beside it.  Rates are over calls back to back (same inputs,
     # same outputs): inside a step, the event in front of the first routing
-    # kernel leaves a few idle microseconds that are no part of routing
-    n_route = 10
-    er = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(5):  # untimed: after the attention calls the caches hold their output
-        buf.route(q, k, v)
-    torch.cuda.synchronize()
-    er[0].record(stream)
-    for _ in range(n_route):
-        buf.route(q, k, v)
-    er[1].record(stream)
-    torch.cuda.synchronize()
-    route_b2b_ms = er[0].elapsed_time(er[1]) / n_route
+    # kernel leaves a few idle microseconds that are no part of routing.
+    route_bytes = 2 * H * N * d * 2 + H * nb * nb * 2 + H * nb * 4 + H * 4 + nb * B * 4
+    kv_bytes = 2 * H * N * d * 2 + 2 * H * nb * B * d * 2 + nb * B * 4
+    fused_bytes = route_bytes + H * N * d * 2 + 2 * H * nb * B * d * 2 + H * nb * nb * 4
+
+    def back_to_back_ms(fn, n=10):
+        er = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(5):  # untimed: after the attention calls the caches hold their output
+            fn()
+        torch.cuda.synchronize()
+        er[0].record(stream)
+        for _ in range(n):
+            fn()
+        er[1].record(stream)
+        torch.cuda.synchronize()
+        return er[0].elapsed_time(er[1]) / n
+
+    def hbm(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bytes": nbytes, "ms_back_to_back": round(ms, 4), "GB/s": round(gbs, 1),
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    rbuf = F.Buffers.allocate(prob)
+    route_b2b_ms = back_to_back_ms(lambda: rbuf.route(q, k, with_scores=False))
+    if not (torch.equal(rbuf.ranked, buf.ranked) and torch.equal(rbuf.row_count, buf.row_count)):
+        raise RuntimeError("routing alone decided differently from the fused pass")
+    fused_ms = back_to_back_ms(lambda: buf.route(q, k, v))
+    kv_ms = back_to_back_ms(lambda: rbuf.kv_layout(k, v))
+    del rbuf
     route_gbs = route_bytes / (route_b2b_ms * 1e-3) / 1e9
 
     # one-GPU analog of the load-imbalance factor: work list-scheduled onto the
@@ -490,6 +551,14 @@ def main():
     ideal_cu = costs.sum() / cus
     per_cu = {"planned": round(list_schedule_makespan(it_cost, cus) / ideal_cu, 4),
               "natural": round(list_schedule_makespan(costs, cus) / ideal_cu, 4)}
+
+    # measured imbalance: one traced attention launch (bitwise the same call,
+    # per-item clocks), next to the list-scheduling estimate above
+    trace = torch.empty((int(meta[0]), F.fva.FVA_TRACE_FIELDS), dtype=torch.int64, device="cuda")
+    buf.attn(q, item_trace=trace)
+    torch.cuda.synchronize()
+    measured = measured_cu_imbalance(trace.cpu().numpy(), workers)
+    del trace
 
     # GSRS precise block importance (phase 1 inside the attention call, phase
     # 2 as its own kernel): cost over the plain attention call
@@ -589,7 +658,8 @@ def main():
     cpu = None
     if not args.skip_cpu_baseline:
         gpu_o = buf.o.float().cpu().numpy().astype(np.float64)
-        cpu = cpu_baseline(wl, inp, p, gpu_o, row_ptr, col_idx, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, p, gpu_o, row_ptr, col_idx, args.cpu_seconds,
+                           all_tiles=wl.name == "rank480p")
 
     out = {
         "metric": METRIC,
@@ -620,8 +690,13 @@ def main():
                "host_wall_per_step": round(wall / K * 1e3, 4),
                "note": "attn from the timed region; route, plan and step_* from a second pass of the "
                        "same steps with an event between every two phases"},
-        "route_hbm": {"bytes": route_bytes, "ms_back_to_back": round(route_b2b_ms, 4),
-                      "GB/s": round(route_gbs, 1), "frac": round(route_gbs / PEAK_HBM_GBS, 4)},
+        "route_hbm": dict(hbm(route_bytes, route_b2b_ms),
+                          what="routing alone: Q, K read; ranking, counts, order written"),
+        "route_fused_hbm": dict(hbm(fused_bytes, fused_ms),
+                                what="the step's routing pass: routing + scores exported + K/V "
+                                     "re-laid out for the attention (V read, K and V written)"),
+        "kv_layout_hbm": dict(hbm(kv_bytes, kv_ms),
+                              what="K/V re-layout alone (fva_kv_layout): K, V read, written"),
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
@@ -635,7 +710,7 @@ def main():
         "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
                          "planned": round(planned / ideal, 4), "lpt_whole_tiles": round(lpt / ideal, 4),
                          "natural": round(natural / ideal, 4), "compute_units": cus,
-                         "per_compute_unit": per_cu},
+                         "per_compute_unit": per_cu, "measured": measured},
         "dense_reference": dense,
         "balance": balance,
         "gsrs": gsrs,

@@ -5,12 +5,17 @@
  * One call of the hot path is three stream-ordered entry points:
  *
  *   fva_route            video-aware order, pooled Q/K block scores, ranking,
- *                        Top-p cutoff with a Top-k floor, per-head counts,
- *                        K and V re-laid out in the order
+ *                        Top-p cutoff with a Top-k floor, per-head counts;
+ *                        optionally also K and V re-laid out in the order
  *   fva_plan             refill of next-ranked blocks, CSR block mask,
  *                        heaviest-first (LPT) tile order, queue reset
  *   fva_sparse_attn_fwd  block-sparse attention forward over the kept blocks,
  *                        run from a persistent tile queue
+ *
+ * Attention over a mask the caller already holds (a reused or hand-built
+ * CSR) needs no routing: fva_kv_layout puts the caller's K and V into the
+ * layout the attention reads, and fva_schedule builds the work list of any
+ * CSR mask.
  *
  * Sources (page title, section) for what each call computes:
  *   "FVAttn: Adaptive Sparse Attention with Runtime Load Balancing for Video
@@ -121,7 +126,8 @@ typedef struct fva_sizes_t {
   int64_t scores_elems;      /* H*nb*nb float (scores) */
   int64_t ranked_elems;      /* H*nb*nb int16 (ranked) */
   int64_t col_idx_capacity;  /* H*nb*nb int32 (col_idx, worst case) */
-  int64_t workspace_bytes;   /* fva_route workspace */
+  int64_t workspace_bytes;   /* fva_route workspace (pooled means, and the
+                                scores when the caller passes none) */
   int32_t tile_counter_elems;/* 2 uint32 */
   int64_t kv_elems;          /* 2*H*nb*B*d bf16 (kv) */
   int64_t work_order_elems;  /* H*nb + min(H*nb, FVA_MAX_SPLITS) int32 (work_order) */
@@ -146,10 +152,12 @@ int fva_compute_units(int32_t* out);
 
 /*
  * Routing frontend (FVAttn S3.1; GSRS S5.3, A.4, A.6).
- *   q, k, v     device bf16 [H][N][d] (strided as above), read only.
- *   scores      device float [H][nb][nb], written: s_{h,i,j} =
+ *   q, k        device bf16 [H][N][d] (strided as above), read only.
+ *   v           device bf16 [H][N][d] or NULL; given exactly when kv is.
+ *   scores      device float [H][nb][nb] or NULL, written: s_{h,i,j} =
  *               sm_scale * <mean of Q_h over query block i, mean of K_h over
- *               key block j>, blocks taken in the video-aware order.
+ *               key block j>, blocks taken in the video-aware order.  With
+ *               NULL the scores live in the workspace and are not returned.
  *   ranked      device int16 [H][nb][nb], written: per row, key-block ids by
  *               float32 score descending, equal scores by lower id.
  *   row_count   device int32 [H*nb], written: k_i = max(k_p, min(k_min, nb))
@@ -163,21 +171,38 @@ int fva_compute_units(int32_t* out);
  *               tile_h x tile_w tiles in raster order, raster inside a tile,
  *               edge tiles cut at the border).
  *   kv          device bf16 [2][H][nb*B][d] (fva_sizes().kv_elems), 16-byte
- *               aligned, written: K and V of every head permuted into the
- *               order (GSRS A.6: the permutation that makes blocks
- *               contiguous), the layout fva_sparse_attn_fwd reads.  Part 0:
- *               row p of head h = K row of token order[p]; part 1: V
- *               transposed per 64-position sub-block s, [h][s][c][j] = V of
- *               token order[64 s + key(j)] at feature c, with
- *               key(j) = 16(j/16) + 8((j%8)/4) + 4((j/8)%2) + j%4.  Rows of
- *               positions past N are zero.
+ *               aligned, or NULL: when given, the routing pass also writes
+ *               exactly what fva_kv_layout(k, v) writes (K is read once for
+ *               both the pooling and the re-layout).  NULL makes the call
+ *               routing only: it reads Q and K and nothing else.
  *   workspace   device scratch of workspace_bytes >= fva_sizes().workspace_bytes
- *               (pooled block means); contents are not needed after the call.
+ *               (pooled block means, and the scores when scores is NULL);
+ *               contents are not needed after the call.
+ * FVA_ERR_ARG also when exactly one of v and kv is NULL.
  */
 int fva_route(const fva_problem* prob, const void* q, const void* k,
               const void* v, float* scores, int16_t* ranked,
               int32_t* row_count, int32_t* head_count, int32_t* order,
               void* kv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * K and V in the layout fva_sparse_attn_fwd reads (GSRS A.6: the token
+ * permutation that makes every block a contiguous run of positions).
+ *   k, v        device bf16 [H][N][d] (strided as above), read only.
+ *   order       device int32 [nb*B], written: as fva_route's order.
+ *   kv          device bf16 [2][H][nb*B][d] (fva_sizes().kv_elems), 16-byte
+ *               aligned, written.  Part 0: row p of head h = K row of token
+ *               order[p]; part 1: V transposed per 64-position sub-block s,
+ *               [h][s][c][j] = V of token order[64 s + key(j)] at feature c,
+ *               with key(j) = 16(j/16) + 8((j%8)/4) + 4((j/8)%2) + j%4 (the
+ *               order in which the attention's score accumulators hold their
+ *               keys, so that its V operand is one 16-byte load).  Rows of
+ *               positions past N are zero.
+ * Depends only on K, V and the problem's geometry: a caller that keeps a
+ * mask across calls (GSRS S5.1 mask reuse) calls this instead of fva_route.
+ */
+int fva_kv_layout(const fva_problem* prob, const void* k, const void* v,
+                  int32_t* order, void* kv, void* stream);
 
 /*
  * Plan (FVAttn S3.2-S3.3 on one GPU: the placement step becomes a
@@ -220,14 +245,34 @@ int fva_plan(const fva_problem* prob, const int16_t* ranked,
              int32_t* plan_meta, uint32_t* tile_counter, void* stream);
 
 /*
+ * The placement step of fva_plan on its own, for a CSR mask the caller
+ * already holds (FVAttn S3.2: placement changes where work runs, never which
+ * blocks are computed).
+ *   row_ptr      device int32 [H*nb + 1], read only: CSR row offsets, each
+ *                row keeping between 1 and nb blocks.
+ *   work_order, plan_meta, tile_counter   written exactly as fva_plan writes
+ *                them for a mask with these row lengths (same split rule,
+ *                same heaviest-first order).
+ * Queries the device for C (FVA_ERR_HIP without one).
+ */
+int fva_schedule(const fva_problem* prob, const int32_t* row_ptr,
+                 int32_t* work_order, int32_t* plan_meta,
+                 uint32_t* tile_counter, void* stream);
+
+/*
  * Block-sparse attention forward (GSRS S3.2, A.1): for every query token of
  * query block i of head h, softmax(sm_scale * q.k) over the tokens of the kept
  * key blocks col_idx[row_ptr[h*nb+i] .. row_ptr[h*nb+i+1]) only, times V.
  *   q            device bf16 [H][N][d] (strided as above), read only.
- *   kv           K and V as written by fva_route, read only.
+ *   kv           K and V as written by fva_kv_layout (or by fva_route
+ *                with a kv buffer), read only.
  *   order        device int32 [nb*B] as written by fva_route.
- *   row_ptr, col_idx   CSR mask (each row non-empty, ids in [0, nb)).
- *   work_order, plan_meta   as written by fva_plan; the queue hands the
+ *   row_ptr, col_idx   CSR mask: each row keeps between 1 and nb blocks,
+ *                ids in [0, nb).  A mask outside this contract gives
+ *                unspecified o and lse (the K/V loads stay inside the kv
+ *                buffer whatever the ids).
+ *   work_order, plan_meta   as written by fva_plan or fva_schedule (for
+ *                this row_ptr); the queue hands the
  *                work items out in work_order's order.  Any permutation of
  *                the first plan_meta[0] entries gives bitwise the same o and
  *                lse.  The two parts of a split tile each leave their
@@ -258,6 +303,28 @@ int fva_sparse_attn_fwd(const fva_problem* prob, const void* q, const void* kv,
                         const int32_t* plan_meta, uint32_t* tile_counter,
                         void* o, float* lse, float* block_lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * fva_sparse_attn_fwd with a per-work-item trace, for measuring how the
+ * persistent queue spreads work over the compute units (the one-GPU form of
+ * FVAttn S2.2 Eq 2's imbalance factor).  Same arguments and outputs, plus:
+ *   item_trace   device int64 [plan_meta[0]][FVA_TRACE_FIELDS], written: for
+ *                the work item at queue position x, [x][0] and [x][1] the
+ *                constant-rate clock (100 MHz) when its workgroup started and
+ *                finished it, [x][2] and [x][3] the compute unit's own cycle
+ *                counter at the same two points, [x][4] the hardware placement
+ *                of the workgroup (XCC id << 32 | hardware id register), and
+ *                [x][5] the workgroup index.
+ * The trace stores are the only difference from fva_sparse_attn_fwd: o, lse
+ * and block_lse are bitwise the same.
+ */
+#define FVA_TRACE_FIELDS 6
+int fva_sparse_attn_fwd_traced(const fva_problem* prob, const void* q, const void* kv,
+                               const int32_t* order, const int32_t* row_ptr,
+                               const int32_t* col_idx, const int32_t* work_order,
+                               const int32_t* plan_meta, uint32_t* tile_counter,
+                               void* o, float* lse, float* block_lse, void* workspace,
+                               size_t workspace_bytes, int64_t* item_trace, void* stream);
 
 /*
  * Precise block importance (GSRS S5.3 phase 2, A.2): after an attention call
@@ -339,7 +406,7 @@ int fva_gsrs_action(const fva_gsrs_schedule* schedule, int32_t step,
                     int32_t* action, float* top_p);
 
 /*
- * Diagnostic (not part of the hot path): enqueue a kernel that runs only
+ * Measurement aid, outside the hot path: enqueue a kernel that runs only
  * bf16 MFMAs (v_mfma_f32_32x32x16_bf16, four independent chains per wave,
  * two 256-thread workgroups per compute unit) for `iters` rounds, with zero
  * operands (random_operands = 0) or N(0,1)-like ones (1).  The caller times

@@ -67,7 +67,8 @@ def test_sizes_of_the_480p_share():
     assert s.num_blocks == 256 and s.num_rows == 1280
     assert s.order_elems == 256 * 128
     assert s.scores_elems == 5 * 256 * 256 == s.ranked_elems == s.col_idx_capacity
-    assert s.workspace_bytes == 2 * 5 * 256 * 128 * 4
+    # pooled means, then room for the scores when the caller passes none
+    assert s.workspace_bytes == 2 * 5 * 256 * 128 * 4 + 5 * 256 * 256 * 4
     assert s.tile_counter_elems == 2
 
 
@@ -114,6 +115,12 @@ def test_entry_points_reject_null_pointers_without_a_device():
     assert st == fva.FVA_ERR_ARG
     st = lib.fva_sparse_attn_fwd(ctypes.byref(p), *([null] * 12), 0, null)
     assert st == fva.FVA_ERR_ARG
+    st = lib.fva_sparse_attn_fwd_traced(ctypes.byref(p), *([null] * 12), 0, null, null)
+    assert st == fva.FVA_ERR_ARG
+    st = lib.fva_kv_layout(ctypes.byref(p), *([null] * 5))
+    assert st == fva.FVA_ERR_ARG
+    st = lib.fva_schedule(ctypes.byref(p), *([null] * 5))
+    assert st == fva.FVA_ERR_ARG
     st = lib.fva_block_importance(ctypes.byref(p), *([null] * 7))
     assert st == fva.FVA_ERR_ARG
     assert lib.fva_sizes(None, None) == fva.FVA_ERR_ARG
@@ -145,6 +152,41 @@ def test_route_rejects_small_workspace_before_launch():
     st = lib.fva_route(ctypes.byref(p), *([fake] * 8), ctypes.c_void_p((1 << 20) + 8), fake,
                        1 << 30, None)
     assert st == fva.FVA_ERR_ARG
+
+
+def test_route_optional_outputs():
+    """v and kv come together (routing only without them); scores may be NULL.
+    Checked on the host: each call below fails on the workspace size, which
+    is tested after the pointers."""
+    lib = F.load_library()
+    p = _ok_problem()
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(v=fake, scores=fake, kv=fake):
+        # q k v scores ranked row_count head_count order kv workspace bytes stream
+        return lib.fva_route(ctypes.byref(p), fake, fake, v, scores, fake, fake, fake, fake, kv, fake,
+                             16, None)
+
+    assert call() == fva.FVA_ERR_WORKSPACE
+    assert call(v=None, kv=None) == fva.FVA_ERR_WORKSPACE
+    assert call(scores=None) == fva.FVA_ERR_WORKSPACE
+    assert call(v=None, kv=None, scores=None) == fva.FVA_ERR_WORKSPACE
+    assert call(v=None) == fva.FVA_ERR_ARG
+    assert call(kv=None) == fva.FVA_ERR_ARG
+
+
+def test_kv_layout_and_schedule_argument_checks():
+    lib = F.load_library()
+    p = _ok_problem()
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.fva_kv_layout(ctypes.byref(p), mis, fake, fake, fake, None) == fva.FVA_ERR_ARG
+    assert lib.fva_kv_layout(ctypes.byref(p), fake, fake, fake, mis, None) == fva.FVA_ERR_ARG
+    assert lib.fva_kv_layout(ctypes.byref(p), fake, fake, None, fake, None) == fva.FVA_ERR_ARG
+    bad = _ok_problem(k_min=0)
+    assert lib.fva_kv_layout(ctypes.byref(bad), fake, fake, fake, fake, None) == fva.FVA_ERR_ARG
+    assert lib.fva_schedule(ctypes.byref(bad), fake, fake, fake, fake, None) == fva.FVA_ERR_ARG
+    assert lib.fva_schedule(ctypes.byref(p), fake, None, fake, fake, None) == fva.FVA_ERR_ARG
 
 
 def test_sizes_of_kv_plan_and_attention_buffers():
@@ -183,6 +225,11 @@ def test_attention_argument_checks_before_launch():
     st = lib.fva_sparse_attn_fwd(ctypes.byref(p), fake, fake, *([fake] * 6), fake, None, fake, fake,
                                  need, None)
     assert st == fva.FVA_ERR_ARG
+    # the traced call needs an 8-byte aligned trace buffer
+    for trace in (None, ctypes.c_void_p((1 << 20) + 4)):
+        st = lib.fva_sparse_attn_fwd_traced(ctypes.byref(p), fake, fake, *([fake] * 6), fake, None,
+                                            None, fake, need, trace, None)
+        assert st == fva.FVA_ERR_ARG
 
 
 def test_order_kind_and_reserved_are_checked():

@@ -100,13 +100,23 @@ def test_padded_token_rows(case):
     prob = problem_for(wl, p, stride_head=N * width, stride_token=width)
     buf = F.Buffers.allocate(prob)
     sentinel = torch.tensor(12345.0, dtype=torch.bfloat16)
-    buf.o = torch.full((Hh, N, width), sentinel.item(), dtype=torch.bfloat16, device="cuda")
+    # the allocated o follows the problem's strides; the padding between its
+    # rows (storage outside the view) is filled to see that nothing writes it
+    assert buf.o.shape == (Hh, N, dd) and buf.o.stride() == (N * width, width, 1)
+    n_storage = buf.o.untyped_storage().nbytes() // 2
+    o_storage = buf.o.as_strided((n_storage,), (1,))
+    o_storage.fill_(sentinel.item())
     buf.run(qp, kp, vp)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(buf.o[:, :, :dd].float().cpu().numpy(), ref["o"])
+    np.testing.assert_array_equal(buf.o.float().cpu().numpy(), ref["o"])
     np.testing.assert_array_equal(buf.lse.cpu().numpy(), ref["lse"].astype(np.float32))
     np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
-    assert bool((buf.o[:, :, dd:] == sentinel.item()).all()), "padding was written"
+    in_view = np.zeros(n_storage, bool)
+    offs = (np.arange(Hh)[:, None, None] * N * width + np.arange(N)[None, :, None] * width
+            + np.arange(dd)[None, None, :])
+    in_view[offs.ravel()] = True
+    outside = o_storage.float().cpu().numpy()[~in_view]
+    assert outside.size > 0 and bool((outside == sentinel.item()).all()), "padding was written"
 
 
 def _scaled_bits(bits: np.ndarray, pow2: int) -> np.ndarray:

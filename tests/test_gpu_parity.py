@@ -23,7 +23,11 @@ from synth.workloads import WORKLOAD_ORDER
 pytestmark = pytest.mark.gpu
 
 CASES = [(name, p) for name in WORKLOAD_ORDER for p in WORKLOADS[name].top_p]
-FULL_ATTENTION = {"tiny", "two_head"}
+# attention compared on every tile (the 480p share: 1,280 tiles, ~20 s of fp64
+# on the host); the two larger workloads on >= 64 seeded tiles per head plus
+# each head's heaviest, lightest and last tile
+FULL_ATTENTION = {"tiny", "two_head", "rank480p"}
+SAMPLED_PER_HEAD = 64
 
 
 def _oracle_scores(wl, inp, order=None):
@@ -103,7 +107,8 @@ def test_chain_matches_oracle(name, p):
     if name in FULL_ATTENTION:
         check_attention(wl, inp, res, label="all tiles:")
     else:
-        tiles = sample_tiles(res["row_ptr"], wl.num_heads, res["nb"], per_head=12, seed=7)
+        tiles = sample_tiles(res["row_ptr"], wl.num_heads, res["nb"], per_head=SAMPLED_PER_HEAD, seed=7)
+        assert len(tiles) >= SAMPLED_PER_HEAD * wl.num_heads
         check_attention(wl, inp, res, tiles, label=f"{len(tiles)} sampled tiles:")
 
 
@@ -206,10 +211,10 @@ def test_token_major_layout_matches_head_major():
     prob = problem_for(wl, wl.top_p[0], stride_head=d, stride_token=H * d)
     import adaptive_block_sparse_fva_amd as F
     buf = F.Buffers.allocate(prob)
-    buf.o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    assert buf.o.stride() == (d, H * d, 1)  # o allocated with the problem's strides
     buf.run(qt, kt, vt)
     torch.cuda.synchronize()
-    got = buf.o.permute(1, 0, 2).float().cpu().numpy()
+    got = buf.o.float().cpu().numpy()
     np.testing.assert_array_equal(got, ref["o"])
     np.testing.assert_array_equal(buf.row_ptr.cpu().numpy(), ref["row_ptr"])
 
