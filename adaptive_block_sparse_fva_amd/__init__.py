@@ -25,6 +25,7 @@ from .fva import (  # noqa: F401
     plan,
     reselect,
     route,
+    route_noalloc,
     schedule,
     sasa_refill,
     sizes,

@@ -159,6 +159,33 @@ static int split_rule(int cus) {
   return split_s < 1 ? 1 : split_s;
 }
 
+// Routing workspace of fva_route_noalloc: one static array per device (each
+// GPU holds its own copy).  Host code never passes `scratch` itself to a
+// kernel: in host code the name is a stand-in, not a device address.  The
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[FVA_NOALLOC_SCRATCH_BYTES];
+static void* g_scratch_ptr[64];
+
+// Device address of the current device's scratch array, resolved on first
+// use; FVA_OK or FVA_ERR_HIP.
+static int scratch_address(void** out) {
+  int dev = 0;
+  int st = record_hip_error(hipGetDevice(&dev), "hipGetDevice");
+  if (st) return st;
+  if (dev < 0 || dev >= 64) return FVA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    st = record_hip_error(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st) return st;
+    if (ptr == nullptr) return record_hip_error(hipErrorInvalidSymbol, "scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FVA_OK;
+}
+
 static float effective_scale(const fva_problem* p) {
   return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
 }
@@ -240,6 +267,27 @@ int fva_route(const fva_problem* prob, const void* q, const void* k, const void*
   float* qbar = (float*)workspace;
   float* kbar = qbar + (int64_t)prob->num_heads * nb * prob->head_dim;
   if (scores == nullptr) scores = (float*)((char*)workspace + pooled_bytes(prob, nb));
+  return launch_route(*prob, nb, q, k, v, scores, ranked, row_count, head_count, order, kv, qbar,
+                      kbar, effective_scale(prob), (hipStream_t)stream);
+}
+
+int fva_route_noalloc(const fva_problem* prob, const void* q, const void* k, const void* v,
+                      float* scores, int16_t* ranked, int32_t* row_count, int32_t* head_count,
+                      int32_t* order, void* kv, void* stream) {
+  int nb = 0;
+  int st = check_problem(prob, &nb);
+  if (st) return st;
+  if (!q || !k || !ranked || !row_count || !head_count || !order) return FVA_ERR_ARG;
+  if ((v == nullptr) != (kv == nullptr)) return FVA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k)) return FVA_ERR_ARG;
+  if (kv && (!aligned16(v) || !aligned16(kv))) return FVA_ERR_ARG;
+  if (workspace_need(prob, nb) > (int64_t)FVA_NOALLOC_SCRATCH_BYTES) return FVA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  float* qbar = (float*)ws;
+  float* kbar = qbar + (int64_t)prob->num_heads * nb * prob->head_dim;
+  if (scores == nullptr) scores = (float*)((char*)ws + pooled_bytes(prob, nb));
   return launch_route(*prob, nb, q, k, v, scores, ranked, row_count, head_count, order, kv, qbar,
                       kbar, effective_scale(prob), (hipStream_t)stream);
 }

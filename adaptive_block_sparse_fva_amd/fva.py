@@ -46,12 +46,14 @@ FVA_GSRS_FULL_SEARCH = 1
 FVA_GSRS_CANDIDATE_SEARCH = 2
 FVA_GSRS_REUSE = 3
 FVA_TRACE_FIELDS = 6
+FVA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = (
     "fva_sizes",
     "fva_attn_workgroups",
     "fva_compute_units",
     "fva_route",
+    "fva_route_noalloc",
     "fva_kv_layout",
     "fva_plan",
     "fva_schedule",
@@ -170,6 +172,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_attn_workgroups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.fva_compute_units.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.fva_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fva_route_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_kv_layout.argtypes = [P, vp, vp, vp, vp, vp]
     lib.fva_plan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fva_schedule.argtypes = [P, vp, vp, vp, vp, vp]
@@ -192,7 +195,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_last_error.restype = ctypes.c_char_p
     lib.fva_version.argtypes = []
     for name in ("fva_sizes", "fva_attn_workgroups", "fva_compute_units", "fva_route",
-                 "fva_kv_layout", "fva_plan", "fva_schedule", "fva_sparse_attn_fwd",
+                 "fva_route_noalloc", "fva_kv_layout", "fva_plan", "fva_schedule", "fva_sparse_attn_fwd",
                  "fva_sparse_attn_fwd_traced", "fva_block_importance", "fva_mfma_probe",
                  "fva_balance", "fva_sasa_refill", "fva_reselect", "fva_gsrs_action", "fva_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -269,6 +272,15 @@ def route(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, works
                                   _ptr(kv), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "fva_route")
+
+
+def route_noalloc(prob, q, k, v, scores, ranked, row_count, head_count, order, kv, stream=None):
+    """fva_route_noalloc: fva_route with the workspace in the library's own static
+    device array (no allocation); v and kv may both be None, scores may be None."""
+    st = load_library().fva_route_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(scores), _ptr(ranked), _ptr(row_count),
+                                          _ptr(head_count), _ptr(order), _ptr(kv), _stream(stream))
+    _check(st, "fva_route_noalloc")
 
 
 def kv_layout(prob, k, v, order, kv, stream=None):

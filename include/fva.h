@@ -186,6 +186,24 @@ int fva_route(const fva_problem* prob, const void* q, const void* k,
               void* kv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fva_route for callers that cannot allocate device memory (code under HIP
+ * stream capture, serving loops or harnesses that forbid allocation): the
+ * same arguments without the workspace, which lives instead in a static
+ * device array of FVA_NOALLOC_SCRATCH_BYTES that each GPU the library runs
+ * on holds until the process ends.  The call allocates and frees nothing.
+ * Problems whose fva_sizes().workspace_bytes exceed the array return
+ * FVA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * that GPU's one array: calls that may overlap on one GPU (other streams,
+ * other host threads) race on it and must be ordered by the caller.
+ * Outputs exactly as fva_route's.
+ */
+#define FVA_NOALLOC_SCRATCH_BYTES (32 << 20)
+int fva_route_noalloc(const fva_problem* prob, const void* q, const void* k,
+                      const void* v, float* scores, int16_t* ranked,
+                      int32_t* row_count, int32_t* head_count, int32_t* order,
+                      void* kv, void* stream);
+
+/*
  * K and V in the layout fva_sparse_attn_fwd reads (GSRS A.6: the token
  * permutation that makes every block a contiguous run of positions).
  *   k, v        device bf16 [H][N][d] (strided as above), read only.
