@@ -154,9 +154,6 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t k_lds3[NBUF > 3 ? TILE : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t v_lds3[NBUF > 3 ? TILE : 8];
   __shared__ int s_tile;
-  // the tile's kept key-block list, staged once per tile so that the per-step
-  // position lookups are LDS broadcasts rather than global loads
-  __shared__ int s_cols[FVA_MAX_BLOCKS];
   auto kslot = [&](auto b) -> bf16_t* {
     constexpr int B = decltype(b)::value;
     if constexpr (B == 0) return k_lds0;
@@ -262,10 +259,13 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       }
     }
     const int nsub = ncols * SUB;
-    for (int c = tid; c < ncols; c += BLK * 2) s_cols[c] = a.col_idx[c0 + c];
-    __syncthreads();
-    // first sequence position of sub-block u
-    auto sub_pos = [&](int u) { return s_cols[u / SUB] * BLK + (u % SUB) * KB; };
+    // first sequence position of sub-block u; the kept key-block ids come
+    // through the scalar cache (uniform addresses in the constant address
+    // space: the list is not written while the kernel runs), so no LDS copy
+    // of the list and no vector load stands before a step's first MFMA
+    typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+    const const_i32p cols = (const_i32p)(a.col_idx + c0);
+    auto sub_pos = [&](int u) { return cols[u / SUB] * BLK + (u % SUB) * KB; };
 
     // K and V^T sub-tiles of sub-block u: both start at byte pos * D * 2 of
     // their head's re-laid-out buffer
@@ -460,7 +460,7 @@ void sparse_attn_fwd_kernel(AttnArgs a) {
       }
     }
     if (tid == 0) s_tile = (int)gridDim.x + (int)atomicAdd(&a.tile_counter[0], 1u);
-    __syncthreads();  // every wave is past its last use of s_cols; s_tile is set
+    __syncthreads();  // s_tile is set
     idx = s_tile;
     __syncthreads();
   }
