@@ -9,7 +9,6 @@
 // re-scoring); here every row gets e_i = min(nb - k_i, k_i * f / 1000), with
 // f one value for the call or one per head (a budget turned into a refill).
 #include "fva_common.h"
-#include "fva_lanes.h"
 
 namespace fva {
 
@@ -30,67 +29,6 @@ __device__ __forceinline__ int row_refill(const int32_t* __restrict__ head_refil
 // Sort key of a work item: length descending, then tile, then part.
 __device__ __forceinline__ uint32_t item_key(int len, int tile, int part) {
   return ((uint32_t)(FVA_MAX_BLOCKS - len) << 15) | ((uint32_t)tile << 1) | (uint32_t)part;
-}
-
-// NS consecutive stages of bitonic merge level kk, compare distances jj,
-// jj/2, .., jj >> (NS-1), done as one round: the 2^NS elements whose indices
-// differ only in those NS bits form a group that the stages never leave, and
-// they share the level's direction bit (kk lies above jj), so a thread loads
-// a group into registers, applies the NS stages in order and writes it back.
-// Same compare-exchanges as the stage-by-stage network, one LDS round trip
-// and one barrier per round.
-template <int NS>
-__device__ __forceinline__ void sort_round(uint32_t* keys, int ipad, int kk, int jj, int tid) {
-  constexpr int G = 1 << NS;
-  const int low = jj >> (NS - 1);
-  for (int g = tid; g < (ipad >> NS); g += PLAN_THREADS) {
-    const int base = ((g & ~(low - 1)) << NS) | (g & (low - 1));
-    const bool asc = (base & kk) == 0;
-    uint32_t v[G];
-#pragma unroll
-    for (int m = 0; m < G; ++m) v[m] = keys[base + m * low];
-#pragma unroll
-    for (int st = NS - 1; st >= 0; --st)
-#pragma unroll
-      for (int m = 0; m < G; ++m)
-        if (!(m & (1 << st))) {
-          const uint32_t a = v[m], b = v[m | (1 << st)];
-          const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
-          v[m] = asc ? lo : hi;
-          v[m | (1 << st)] = asc ? hi : lo;
-        }
-#pragma unroll
-    for (int m = 0; m < G; ++m) keys[base + m * low] = v[m];
-  }
-  __syncthreads();
-}
-
-// Stages J0, J0/2, .., 1 of bitonic merge level kk on one wave's chunk of
-// 128 keys at offset base, held two per lane (chunk slot 64e + lane in
-// v[e]): distance 64 pairs a lane's two keys, smaller distances pair lanes
-// (DPP / permlane exchanges).  Every such stage stays inside the chunk.
-template <int J0>
-__device__ __forceinline__ void chunk_stages(uint32_t (&v)[2], int lane, int base, int kk) {
-  static_for<0, __builtin_ctz(J0) + 1>([&](auto sl) {
-    constexpr int JJ = J0 >> decltype(sl)::value;
-    if constexpr (JJ == 64) {
-      const bool asc = ((base + lane) & kk) == 0;
-      const uint32_t x = v[0], y = v[1];
-      const bool keep = (x < y) == asc;  // the pair is already in this chunk's order
-      v[0] = keep ? x : y;
-      v[1] = keep ? y : x;
-    } else {
-      const bool lower = (lane & JJ) == 0;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bool asc = ((base + 64 * e + lane) & kk) == 0;
-        const uint32_t a = v[e], b = xor_lane<JJ>(a);
-        // the lower side of an ascending pair keeps the smaller key: one
-        // compare picks between a and b
-        v[e] = ((a < b) == (lower == asc)) ? a : b;
-      }
-    }
-  });
 }
 
 // One workgroup: final counts, CSR row offsets, per-head totals, the split
@@ -115,9 +53,9 @@ __device__ __forceinline__ void plan_scan(
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_count_final,
     int32_t* __restrict__ work_order, int32_t* __restrict__ plan_meta,
     uint32_t* __restrict__ tile_counter) {
-  // at most FVA_MAX_TILES + FVA_MAX_SPLITS - 1 items, padded to a power of two
-  static_assert(FVA_MAX_SPLITS <= FVA_MAX_TILES, "item list fits the padded sort");
-  extern __shared__ uint32_t keys[];  // sized by the launch to the padded item count
+  // at most FVA_MAX_TILES + FVA_MAX_SPLITS - 1 items
+  static_assert(FVA_MAX_SPLITS <= FVA_MAX_TILES, "item count bound");
+  extern __shared__ uint32_t keys[];  // two item buffers and the sort's count table, sized by the launch
   __shared__ int32_t wave_tot[PLAN_THREADS / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -168,15 +106,30 @@ __device__ __forceinline__ void plan_scan(
   // split decision and slots
   const int mean = (total + split_s - 1) / split_s;
   auto is_split = [&](int kp) { return kp >= 2 && 2 * kp > mean; };
-  int nsp = 0;
-  for (int r = r0; r < r1; ++r) nsp += is_split(kept(r)) ? 1 : 0;
-  int nsplit = 0;
-  int sp = block_scan(nsp, &nsplit);
+  // no row can be cut when even a full row (nb blocks) stays within half the
+  // mean load: then the slot scan is skipped (one barrier still publishes
+  // the row offsets read below)
+  int nsplit = 0, sp = 0;
+  if (2 * nb > mean) {
+    int nsp = 0;
+    for (int r = r0; r < r1; ++r) nsp += is_split(kept(r)) ? 1 : 0;
+    sp = block_scan(nsp, &nsplit);
+  } else {
+    __syncthreads();
+  }
   if constexpr (!FROM_CSR)
     for (int hh = tid; hh < rows / nb; hh += PLAN_THREADS)
       head_count_final[hh] = row_ptr[(hh + 1) * nb] - row_ptr[hh * nb];
 
-  // work items: tile r's items start at r + (split tiles before r)
+  // work items: tile r's items start at r + (split tiles before r); the
+  // range of their length fields bounds the radix passes below
+  __shared__ uint32_t key_lo, key_hi;
+  if (tid == 0) {
+    key_lo = 0xffffffffu;
+    key_hi = 0u;
+  }
+  __syncthreads();
+  uint32_t my_lo = 0xffffffffu, my_hi = 0u;
   for (int r = r0; r < r1; ++r) {
     const int kp = kept(r);
     const int pos = r + sp;
@@ -185,48 +138,121 @@ __device__ __forceinline__ void plan_scan(
       plan_meta[2 + rows + sp] = r;
       keys[pos] = item_key((kp + 1) >> 1, r, 0);
       keys[pos + 1] = item_key(kp >> 1, r, 1);
+      my_lo = min(my_lo, (uint32_t)(FVA_MAX_BLOCKS - ((kp + 1) >> 1)));
+      my_hi = max(my_hi, (uint32_t)(FVA_MAX_BLOCKS - (kp >> 1)));
       ++sp;
     } else {
       plan_meta[2 + r] = -1;
       keys[pos] = item_key(kp, r, 0);
+      my_lo = min(my_lo, (uint32_t)(FVA_MAX_BLOCKS - kp));
+      my_hi = max(my_hi, (uint32_t)(FVA_MAX_BLOCKS - kp));
     }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    my_lo = min(my_lo, (uint32_t)__shfl_xor((int)my_lo, off, 64));
+    my_hi = max(my_hi, (uint32_t)__shfl_xor((int)my_hi, off, 64));
+  }
+  if (lane == 0) {
+    atomicMin(&key_lo, my_lo);
+    atomicMax(&key_hi, my_hi);
   }
   const int nitems = rows + nsplit;
-  int ipad = 128;
-  while (ipad < nitems) ipad <<= 1;
-  for (int x = nitems + tid; x < ipad; x += PLAN_THREADS) keys[x] = 0xffffffffu;
   __syncthreads();
 
-  // bitonic sort of the item keys, ascending.  Merge levels 2 .. 128 stay
-  // inside 128-key chunks: each wave sorts its chunks in registers.  Every
-  // later level kk runs its stages of distance >= 128 over the whole list in
-  // LDS rounds (sort_round, up to three stages each) and the rest inside the
-  // chunks again, so that the workgroup synchronises only between those.
-  const int nchunks = ipad >> 7;
-  for (int c = wave; c < nchunks; c += PLAN_THREADS / 64) {
-    uint32_t v[2] = {keys[128 * c + lane], keys[128 * c + 64 + lane]};
-    static_for<1, 8>([&](auto kl) {
-      constexpr int KK = 1 << decltype(kl)::value;
-      chunk_stages<KK / 2>(v, lane, 128 * c, KK);
-    });
-    keys[128 * c + lane] = v[0];
-    keys[128 * c + 64 + lane] = v[1];
-  }
-  __syncthreads();
-  for (int kk = 256; kk <= ipad; kk <<= 1) {
-    int jj = kk >> 1;
-    for (; jj >= 512; jj >>= 3) sort_round<3>(keys, ipad, kk, jj, tid);
-    if (jj == 256) sort_round<2>(keys, ipad, kk, 256, tid);
-    else if (jj == 128) sort_round<1>(keys, ipad, kk, 128, tid);
-    for (int c = wave; c < nchunks; c += PLAN_THREADS / 64) {
-      uint32_t v[2] = {keys[128 * c + lane], keys[128 * c + 64 + lane]};
-      chunk_stages<64>(v, lane, 128 * c, kk);
-      keys[128 * c + lane] = v[0];
-      keys[128 * c + 64 + lane] = v[1];
+  // Stable LSD radix sort of the items on their length field (key bits
+  // 15 .. 26, up to three 4-bit digits).  Items enter in index order, which is
+  // (tile, part) order, so items of equal length keep that order, as the full
+  // key order demands.  Per pass: each wave takes 64-item slots, ranks its
+  // items among the slot's items with the same digit from four ballots, and
+  // writes per-digit slot counts; an exclusive scan over (digit, slot) gives
+  // every item its destination.
+  {
+    const int cap = rows + (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS);
+    uint32_t* src = keys;
+    uint32_t* dst = keys + cap;
+    uint32_t* tab = keys + 2 * cap;
+    const int nslots = (nitems + 63) >> 6;
+    const int ntab = 16 * nslots;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    // lanes of this slot whose item digit equals e, from the four digit-bit
+    // ballots b[k] and the valid lanes vm
+    auto lanes_with = [&](const uint64_t (&b)[4], uint64_t vm, uint32_t e) {
+      uint64_t m = vm;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m &= ((e >> k) & 1u) ? b[k] : ~b[k];
+      return m;
+    };
+    // digits above the highest bit in which the length fields differ are the
+    // same for every item: those passes would leave the order as it is
+    const uint32_t diff = key_lo ^ key_hi;
+    const int sig = diff ? 32 - __builtin_clz(diff) : 0;
+    const int end_shift = 15 + ((sig + 3) & ~3);
+    for (int shift = 15; shift < end_shift; shift += 4) {
+      for (int s = wave; s < nslots; s += PLAN_THREADS / 64) {
+        const int i = (s << 6) + lane;
+        const bool valid = i < nitems;
+        const uint32_t d = valid ? (src[i] >> shift) & 15u : 0u;
+        uint64_t b[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[k] = __ballot(valid && ((d >> k) & 1u));
+        // lane e < 16 counts the slot's items with digit e
+        const uint64_t cnt = lanes_with(b, __ballot(valid), (uint32_t)lane);
+        if (lane < 16) tab[lane * nslots + s] = (uint32_t)__popcll(cnt);
+      }
+      __syncthreads();
+      if (ntab <= 16 * 64) {
+        // small table: wave 0 scans it (up to 16 entries per lane)
+        if (wave == 0) {
+          const int per_l = (ntab + 63) >> 6;
+          const int t0 = min(ntab, lane * per_l), t1 = min(ntab, t0 + per_l);
+          int loc = 0;
+          for (int x = t0; x < t1; ++x) loc += (int)tab[x];
+          int incl = loc;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+          }
+          int ex = incl - loc;
+          for (int x = t0; x < t1; ++x) {
+            const int c = (int)tab[x];
+            tab[x] = (uint32_t)ex;
+            ex += c;
+          }
+        }
+      } else {
+        const int per_t = (ntab + PLAN_THREADS - 1) / PLAN_THREADS;
+        const int t0 = min(ntab, tid * per_t), t1 = min(ntab, t0 + per_t);
+        int loc = 0;
+        for (int x = t0; x < t1; ++x) loc += (int)tab[x];
+        int tot = 0;
+        int ex = block_scan(loc, &tot);
+        for (int x = t0; x < t1; ++x) {
+          const int c = (int)tab[x];
+          tab[x] = (uint32_t)ex;
+          ex += c;
+        }
+      }
+      __syncthreads();
+      for (int s = wave; s < nslots; s += PLAN_THREADS / 64) {
+        const int i = (s << 6) + lane;
+        const bool valid = i < nitems;
+        const uint32_t v = valid ? src[i] : 0u;
+        const uint32_t d = (v >> shift) & 15u;
+        uint64_t b[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[k] = __ballot(valid && ((d >> k) & 1u));
+        const uint64_t same = lanes_with(b, __ballot(valid), d);
+        if (valid) dst[tab[d * nslots + s] + __popcll(same & below)] = v;
+      }
+      __syncthreads();
+      uint32_t* t = src;
+      src = dst;
+      dst = t;
     }
-    __syncthreads();
+    for (int x = tid; x < nitems; x += PLAN_THREADS) work_order[x] = (int32_t)(src[x] & 0x7fffu);
   }
-  for (int x = tid; x < nitems; x += PLAN_THREADS) work_order[x] = (int32_t)(keys[x] & 0x7fffu);
   if (tid == 0) {
     plan_meta[0] = nitems;
     plan_meta[1] = nsplit;
@@ -335,12 +361,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void schedule_kernel(
                   plan_meta, tile_counter);
 }
 
-// LDS of the work-list sort: the item count padded to a power of two (>= 128).
+// LDS of the work-list sort: two buffers of the largest item count and the
+// (digit, 64-item slot) count table.
 static size_t sort_lds_bytes(int rows) {
   const int cap = rows + (rows < FVA_MAX_SPLITS ? rows : FVA_MAX_SPLITS);
-  int ipad = 128;
-  while (ipad < cap) ipad <<= 1;
-  return (size_t)ipad * sizeof(uint32_t);
+  return (size_t)(2 * cap + 16 * ((cap + 63) / 64)) * sizeof(uint32_t);
 }
 
 int launch_schedule(const fva_problem& p, int nb, int split_s, const int32_t* row_ptr,
