@@ -284,7 +284,7 @@ int fva_schedule(const fva_problem* prob, const int32_t* row_ptr,
  *   q            device bf16 [H][N][d] (strided as above), read only.
  *   kv           K and V as written by fva_kv_layout (or by fva_route
  *                with a kv buffer), read only.
- *   order        device int32 [nb*B] as written by fva_route.
+ *   order        device int32 [nb*B] as written by fva_route or fva_kv_layout.
  *   row_ptr, col_idx   CSR mask: each row keeps between 1 and nb blocks,
  *                ids in [0, nb).  A mask outside this contract gives
  *                unspecified o and lse (the K/V loads stay inside the kv
