@@ -519,7 +519,7 @@ def main():
     def hbm(nbytes, ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"bytes": nbytes, "ms_back_to_back": round(ms, 4), "GB/s": round(gbs, 1),
-                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "frac_of_copy": round(gbs / copy_gbs, 4)}
 
     rbuf = F.Buffers.allocate(prob)
     plan_b2b_ms = back_to_back_ms(lambda: buf.plan())
@@ -597,6 +597,21 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ceiling[label] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+    # the HBM rate a plain device copy reaches on this machine (1 GiB read and
+    # 1 GiB written per copy): the achievable counterpart of the 8 TB/s peak
+    xa = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    xb = torch.empty_like(xa)
+    xb.copy_(xa)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        xb.copy_(xa)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * xa.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del xa, xb
 
     dense = None
     if not args.skip_dense:
@@ -706,6 +721,7 @@ def main():
                      "algorithmic_flops_per_launch": kept,
                      "timed": "attention call = attention kernel + merge of split tiles",
                      "sustained_mfma_tflops": ceiling,
+                     "sustained_copy_gbs": round(copy_gbs, 1),
                      "frac_of_sustained": round(achieved_tflops / ceiling["random_operands"], 4)},
         "precise_importance": precise,
         "cu_imbalance": {"workgroups": workers, "split_tiles": int(meta[1]),
