@@ -292,10 +292,10 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
 // SEL_ROWS consecutive rows per wave and four waves per workgroup; the sort
 // and the scan use no LDS and no barriers (rows of more than 256 blocks take
 // two waves each, see sort_desc_rows):
-//   - keys (orderable(s_j) << 32) | (2^32-1-j), element x = 64e + lane held
+//   - keys (orderable(s_j) << 32) | (2^32-1-j), slot x = E lane + e held
 //     in register e of the lane, sorted descending by a bitonic network
-//     (strides below 64 between lanes, larger strides between registers):
-//     score descending, equal scores by lower id;
+//     (strides below E between the lane's registers, larger strides between
+//     lanes): score descending, equal scores by lower id;
 //   - weights w_r = rint(exp(s_(r) - s_(0)) * 2^40) in fp64, an exact integer
 //     inclusive scan along the ranking, target T = fl(p * W);
 //   - k_p = 1 + #{r : prefix_r < ceil(T)}, k_i = max(k_p, min(k_min, nb)).
@@ -306,7 +306,10 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
 // ---------------------------------------------------------------------------
 constexpr int SEL_ROWS = 1;
 
-// Bitonic sort of the wave's 64 E keys, descending over slot x = 64e + lane.
+// Bitonic sort of the wave's 64 E keys, descending over slot x = E lane + e:
+// each lane holds E consecutive slots, so the strides below E (which occur in
+// the most stages) compare two registers of one lane, and a stride JJ >= E
+// exchanges between lanes l and l ^ (JJ / E).
 template <int E>
 __device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
   constexpr int LOG = __builtin_ctz(64 * E);
@@ -314,32 +317,58 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
     constexpr int KK = 1 << decltype(kl)::value;
     static_for<0, decltype(kl)::value>([&](auto jl) {
       constexpr int JJ = KK >> (decltype(jl)::value + 1);
-      if constexpr (JJ >= 64) {
-        constexpr int JE = JJ / 64;
+      if constexpr (JJ < E) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          if ((e & JE) == 0) {
-            const bool desc = ((e * 64 + lane) & KK) == 0;
-            const uint64_t a = key[e], b = key[e | JE];
+          if ((e & JJ) == 0) {
+            const bool desc = ((lane * E + e) & KK) == 0;
+            const uint64_t a = key[e], b = key[e | JJ];
             if ((a < b) == desc) {
               key[e] = b;
-              key[e | JE] = a;
+              key[e | JJ] = a;
             }
           }
         }
       } else {
-        const bool lower = (lane & JJ) == 0;
+        constexpr int LJ = JJ / E;
+        // KK > JJ >= E, so the direction is the same for all of the lane's slots
+        const bool keep_larger = ((lane & LJ) == 0) == (((lane * E) & KK) == 0);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const bool desc = ((e * 64 + lane) & KK) == 0;
-          const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
+          const uint64_t a = key[e], b = xor_lane_u64<LJ>(a);
           // the slot keeps the larger key where its side and direction agree,
           // else the smaller: one compare picks between a and b
-          key[e] = ((a > b) == (lower == desc)) ? a : b;
+          key[e] = ((a > b) == keep_larger) ? a : b;
         }
       }
     });
   });
+}
+
+// Inclusive scan of the weights w[e] of slots x = E lane + e (a running sum
+// over the lane's registers, then one scan of the lane totals across the
+// wave); total = the wave's sum.
+template <int E>
+__device__ __forceinline__ void scan_slots(const uint64_t (&w)[E], uint64_t (&prefix)[E], uint64_t& total,
+                                           int lane) {
+  uint64_t run = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    run += w[e];
+    prefix[e] = run;
+  }
+  uint64_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = shfl_up_u64(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const uint64_t before = incl - run;
+#pragma unroll
+  for (int e = 0; e < E; ++e) prefix[e] += before;
+  const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+  const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63);
+  total = ((uint64_t)thi << 32) | tlo;
 }
 
 // Exact integer inclusive scan of the weights along the ranking; returns
@@ -350,20 +379,8 @@ template <int E>
 __device__ __forceinline__ int count_below_target(const uint64_t (&w)[E], const bool (&live)[E],
                                                   float p, int lane) {
   uint64_t prefix[E];
-  uint64_t carry = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    uint64_t incl = w[e];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t y = shfl_up_u64(incl, off);
-      if (lane >= off) incl += y;
-    }
-    prefix[e] = carry + incl;
-    const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
-    const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63);
-    carry += ((uint64_t)thi << 32) | tlo;
-  }
+  uint64_t carry;
+  scan_slots<E>(w, prefix, carry, lane);
   const double target = (double)p * (double)carry;
   const uint64_t tint = (uint64_t)ceil(target);
   int cnt = 0;
@@ -382,7 +399,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = e * 64 + lane;
+    const int x = lane * E + e;
     key[e] = x < nb ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x)) : 0ull;
   }
   sort_desc<E>(key, lane);
@@ -390,7 +407,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
   int16_t* rk = ranked + (int64_t)row * nb;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = e * 64 + lane;
+    const int x = lane * E + e;
     if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
   }
 
@@ -408,7 +425,7 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
     bool live[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int x = e * 64 + lane;
+      const int x = lane * E + e;
       const double sr = (double)from_orderable((uint32_t)(key[e] >> 32));
       live[e] = x < nb;
       w[e] = live[e] ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
@@ -420,10 +437,10 @@ __device__ __forceinline__ int select_row(const float* __restrict__ scores, int 
 
 // Rows of more than 256 blocks are ranked by W = 2 waves together (one wave
 // alone would take 16 or 32 keys per lane through the whole network), two
-// rows per workgroup.  Slot x = 64 (EL v + e) + lane of a row is register e
+// rows per workgroup.  Slot x = 64 EL v + EL lane + e of a row is register e
 // of lane `lane` of the row's wave v (v = 0 .. W-1, EL = E / W keys per
-// lane); the bitonic stages of stride below 64 exchange between lanes,
-// strides 64 .. 32 EL between registers, and stride 64 EL -- the widest
+// lane); the bitonic stages of stride below EL compare registers of one lane,
+// strides EL .. 32 EL exchange between lanes, and stride 64 EL -- the widest
 // stage of the last merge level -- between the row's two waves through LDS.
 constexpr int RANK_WAVES = 2;  // waves per row for rows of more than 256 blocks
 
@@ -438,7 +455,7 @@ struct RowRankLds {
 template <int EL>
 __device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, int v, uint64_t* xbuf) {
   constexpr int LOG = __builtin_ctz(64 * EL * RANK_WAVES);
-  const int x0 = v * EL * 64 + lane;  // slot of register 0
+  const int x0 = v * EL * 64 + lane * EL;  // slot of register 0
   static_for<1, LOG + 1>([&](auto kl) {
     constexpr int KK = 1 << decltype(kl)::value;
     static_for<0, decltype(kl)::value>([&](auto jl) {
@@ -448,36 +465,35 @@ __device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, in
 #pragma unroll
         for (int e = 0; e < EL; ++e) xbuf[(v * EL + e) * 64 + lane] = key[e];
         __syncthreads();
-        const bool lower = (v & WJ) == 0;
+        const bool keep_larger = ((v & WJ) == 0) == ((x0 & KK) == 0);
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
-          const bool desc = ((x0 + e * 64) & KK) == 0;
           const uint64_t a = key[e], b = xbuf[((v ^ WJ) * EL + e) * 64 + lane];
-          key[e] = ((a > b) == (lower == desc)) ? a : b;
+          key[e] = ((a > b) == keep_larger) ? a : b;
         }
         __syncthreads();
-      } else if constexpr (JJ >= 64) {
-        constexpr int JE = JJ / 64;
+      } else if constexpr (JJ < EL) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
-          if ((e & JE) == 0) {
-            const bool desc = ((x0 + e * 64) & KK) == 0;
-            const uint64_t a = key[e], b = key[e | JE];
+          if ((e & JJ) == 0) {
+            const bool desc = ((x0 + e) & KK) == 0;
+            const uint64_t a = key[e], b = key[e | JJ];
             if ((a < b) == desc) {
               key[e] = b;
-              key[e | JE] = a;
+              key[e | JJ] = a;
             }
           }
         }
       } else {
-        const bool lower = (lane & JJ) == 0;
+        constexpr int LJ = JJ / EL;
+        // KK > JJ >= EL, so the direction is the same for all of the lane's slots
+        const bool keep_larger = ((lane & LJ) == 0) == ((x0 & KK) == 0);
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
-          const bool desc = ((x0 + e * 64) & KK) == 0;
-          const uint64_t a = key[e], b = xor_lane_u64<JJ>(a);
+          const uint64_t a = key[e], b = xor_lane_u64<LJ>(a);
           // the slot keeps the larger key where its side and direction agree,
           // else the smaller: one compare picks between a and b
-          key[e] = ((a > b) == (lower == desc)) ? a : b;
+          key[e] = ((a > b) == keep_larger) ? a : b;
         }
       }
     });
@@ -494,11 +510,11 @@ __device__ __forceinline__ int select_row_waves(const float* __restrict__ scores
                                                 float top_p, int k_min, int16_t* __restrict__ ranked, int lane,
                                                 int v, RowRankLds<EL>& sh) {
   const float* s = scores + (int64_t)row * nb;
-  const int x0 = v * EL * 64 + lane;
+  const int x0 = v * EL * 64 + lane * EL;
   uint64_t key[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) {
-    const int x = x0 + e * 64;
+    const int x = x0 + e;
     key[e] = (live_row && x < nb) ? (((uint64_t)orderable(s[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x))
                                   : 0ull;
   }
@@ -508,7 +524,7 @@ __device__ __forceinline__ int select_row_waves(const float* __restrict__ scores
     int16_t* rk = ranked + (int64_t)row * nb;
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
-      const int x = x0 + e * 64;
+      const int x = x0 + e;
       if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
     }
   }
@@ -523,25 +539,17 @@ __device__ __forceinline__ int select_row_waves(const float* __restrict__ scores
     if (v == 0 && lane == 0) sh.top = (uint32_t)(key[0] >> 32);
     __syncthreads();
     const double smax = (double)from_orderable(sh.top);
-    uint64_t prefix[EL];
+    uint64_t w[EL], prefix[EL];
     bool live[EL];
-    uint64_t carry = 0;
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
-      const int x = x0 + e * 64;
+      const int x = x0 + e;
       const double sr = (double)from_orderable((uint32_t)(key[e] >> 32));
       live[e] = live_row && x < nb;
-      uint64_t incl = live[e] ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint64_t y = shfl_up_u64(incl, off);
-        if (lane >= off) incl += y;
-      }
-      prefix[e] = carry + incl;
-      const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
-      const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63);
-      carry += ((uint64_t)thi << 32) | tlo;
+      w[e] = live[e] ? (uint64_t)rint(exp(sr - smax) * 1099511627776.0) : 0ull;  // 2^40
     }
+    uint64_t carry;
+    scan_slots<EL>(w, prefix, carry, lane);
     if (lane == 0) sh.wave_total[v] = carry;
     __syncthreads();
     uint64_t before = 0, total = 0;
@@ -596,7 +604,7 @@ __device__ __forceinline__ int reselect_row(const float* __restrict__ importance
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = e * 64 + lane;
+    const int x = lane * E + e;
     const uint64_t id = (uint64_t)(0xffffffffu - (uint32_t)x);
     if (x >= nb)
       key[e] = 0ull;
@@ -610,7 +618,7 @@ __device__ __forceinline__ int reselect_row(const float* __restrict__ importance
   int16_t* rk = ranked + (int64_t)row * nb;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int x = e * 64 + lane;
+    const int x = lane * E + e;
     if (x < nb) rk[x] = (int16_t)(0xffffffffu - (uint32_t)(key[e] & 0xffffffffull));
   }
 
@@ -626,7 +634,7 @@ __device__ __forceinline__ int reselect_row(const float* __restrict__ importance
     bool live[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      live[e] = e * 64 + lane < c;
+      live[e] = lane * E + e < c;
       const double imp = fmax((double)from_orderable((uint32_t)(key[e] >> 32)), 0.0);
       w[e] = live[e] ? (uint64_t)rint(imp * 1099511627776.0) : 0ull;  // 2^40
     }
