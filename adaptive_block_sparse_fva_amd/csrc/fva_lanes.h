@@ -39,4 +39,26 @@ __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
   return ((uint64_t)xor_lane<M>((uint32_t)(x >> 32)) << 32) | xor_lane<M>((uint32_t)x);
 }
 
+// One bitonic compare-exchange of a 64-bit key with the key of lane l ^ M:
+// the larger of the two where keep_larger, else the smaller.  For M = 16 and
+// 32 the permlane swaps of the key's two halves with themselves leave both
+// keys in every lane (the two results of each swap come from the same pair of
+// lanes, in an order that depends on the lane), and the larger or smaller of
+// a pair does not depend on that order.
+template <int M>
+__device__ __forceinline__ uint64_t exchange_keep(uint64_t a, bool keep_larger) {
+  if constexpr (M == 16 || M == 32) {
+    const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
+    const auto h = M == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                           : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = M == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                           : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const uint64_t x0 = ((uint64_t)h[0] << 32) | l[0], x1 = ((uint64_t)h[1] << 32) | l[1];
+    return ((x0 > x1) == keep_larger) ? x0 : x1;
+  } else {
+    const uint64_t b = xor_lane_u64<M>(a);
+    return ((a > b) == keep_larger) ? a : b;
+  }
+}
+
 }  // namespace fva

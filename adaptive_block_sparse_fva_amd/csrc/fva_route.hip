@@ -331,15 +331,12 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[E], int lane) {
         }
       } else {
         constexpr int LJ = JJ / E;
-        // KK > JJ >= E, so the direction is the same for all of the lane's slots
+        // KK > JJ >= E, so the direction is the same for all of the lane's
+        // slots; the slot keeps the larger key where its side and direction
+        // agree, else the smaller
         const bool keep_larger = ((lane & LJ) == 0) == (((lane * E) & KK) == 0);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint64_t a = key[e], b = xor_lane_u64<LJ>(a);
-          // the slot keeps the larger key where its side and direction agree,
-          // else the smaller: one compare picks between a and b
-          key[e] = ((a > b) == keep_larger) ? a : b;
-        }
+        for (int e = 0; e < E; ++e) key[e] = exchange_keep<LJ>(key[e], keep_larger);
       }
     });
   });
@@ -486,15 +483,12 @@ __device__ __forceinline__ void sort_desc_rows(uint64_t (&key)[EL], int lane, in
         }
       } else {
         constexpr int LJ = JJ / EL;
-        // KK > JJ >= EL, so the direction is the same for all of the lane's slots
+        // KK > JJ >= EL, so the direction is the same for all of the lane's
+        // slots; the slot keeps the larger key where its side and direction
+        // agree, else the smaller
         const bool keep_larger = ((lane & LJ) == 0) == ((x0 & KK) == 0);
 #pragma unroll
-        for (int e = 0; e < EL; ++e) {
-          const uint64_t a = key[e], b = xor_lane_u64<LJ>(a);
-          // the slot keeps the larger key where its side and direction agree,
-          // else the smaller: one compare picks between a and b
-          key[e] = ((a > b) == keep_larger) ? a : b;
-        }
+        for (int e = 0; e < EL; ++e) key[e] = exchange_keep<LJ>(key[e], keep_larger);
       }
     });
   });
