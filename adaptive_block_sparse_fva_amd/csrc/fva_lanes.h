@@ -1,6 +1,8 @@
 // Lane exchanges inside one wave64 without going through LDS.
 #pragma once
 
+#include <type_traits>
+
 #include "fva_common.h"
 
 namespace fva {
@@ -37,6 +39,41 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
 template <int M>
 __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
   return ((uint64_t)xor_lane<M>((uint32_t)(x >> 32)) << 32) | xor_lane<M>((uint32_t)x);
+}
+
+// Inclusive prefix sums over the wave's 64 lanes (lane order): DPP row
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes (a lane whose source
+// lies before its row's start adds 0), then the totals of rows 0..2, read
+// from lanes 15, 31 and 47, added to every lane of the rows after them.
+template <int S>
+__device__ __forceinline__ uint32_t dpp_row_shr(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + S, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+  x += dpp_row_shr<1>(x);
+  x += dpp_row_shr<2>(x);
+  x += dpp_row_shr<4>(x);
+  x += dpp_row_shr<8>(x);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  return x + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x, int lane) {
+  auto shr = [](uint64_t v, auto s) {
+    constexpr int S = decltype(s)::value;
+    return ((uint64_t)dpp_row_shr<S>((uint32_t)(v >> 32)) << 32) | dpp_row_shr<S>((uint32_t)v);
+  };
+  x += shr(x, std::integral_constant<int, 1>{});
+  x += shr(x, std::integral_constant<int, 2>{});
+  x += shr(x, std::integral_constant<int, 4>{});
+  x += shr(x, std::integral_constant<int, 8>{});
+  auto lane_value = [&](int l) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  };
+  const uint64_t r0 = lane_value(15), r1 = lane_value(31), r2 = lane_value(47);
+  return x + (lane >= 16 ? r0 : 0ull) + (lane >= 32 ? r1 : 0ull) + (lane >= 48 ? r2 : 0ull);
 }
 
 // One bitonic compare-exchange of a 64-bit key with the key of lane l ^ M:

@@ -281,12 +281,6 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
 }
 
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
-  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)x, d, 64);
-  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(x >> 32), d, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // ---------------------------------------------------------------------------
 // 3. Ranking and cutoff.  One wave per (query block i, head h) row at a time,
 // SEL_ROWS consecutive rows per wave and four waves per workgroup; the sort
@@ -354,12 +348,7 @@ __device__ __forceinline__ void scan_slots(const uint64_t (&w)[E], uint64_t (&pr
     run += w[e];
     prefix[e] = run;
   }
-  uint64_t incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t y = shfl_up_u64(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const uint64_t incl = wave_incl_scan_u64(run, lane);
   const uint64_t before = incl - run;
 #pragma unroll
   for (int e = 0; e < E; ++e) prefix[e] += before;
@@ -380,11 +369,10 @@ __device__ __forceinline__ int count_below_target(const uint64_t (&w)[E], const 
   scan_slots<E>(w, prefix, carry, lane);
   const double target = (double)p * (double)carry;
   const uint64_t tint = (uint64_t)ceil(target);
+  // the count over the wave, from one ballot per register
   int cnt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += (live[e] && prefix[e] < tint) ? 1 : 0;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(live[e] && prefix[e] < tint));
   return cnt;
 }
 
@@ -556,9 +544,7 @@ __device__ __forceinline__ int select_row_waves(const float* __restrict__ scores
     const uint64_t tint = (uint64_t)ceil((double)p * (double)total);
     int cnt = 0;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) cnt += (live[e] && before + prefix[e] < tint) ? 1 : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    for (int e = 0; e < EL; ++e) cnt += __popcll(__ballot(live[e] && before + prefix[e] < tint));
     if (lane == 0) sh.wave_count[v] = cnt;
     __syncthreads();
     int c = 1;
