@@ -9,6 +9,7 @@
 // re-scoring); here every row gets e_i = min(nb - k_i, k_i * f / 1000), with
 // f one value for the call or one per head (a budget turned into a refill).
 #include "fva_common.h"
+#include "fva_lanes.h"
 
 namespace fva {
 
@@ -62,12 +63,7 @@ __device__ __forceinline__ void plan_scan(
 
   // exclusive scan across the workgroup; *total gets the sum
   auto block_scan = [&](int x, int* total) {
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    const int incl = (int)wave_incl_scan((uint32_t)x, lane);
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int base = 0, tot = 0;
@@ -208,12 +204,7 @@ __device__ __forceinline__ void plan_scan(
           const int t0 = min(ntab, lane * per_l), t1 = min(ntab, t0 + per_l);
           int loc = 0;
           for (int x = t0; x < t1; ++x) loc += (int)tab[x];
-          int incl = loc;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += y;
-          }
+          const int incl = (int)wave_incl_scan((uint32_t)loc, lane);
           int ex = incl - loc;
           for (int x = t0; x < t1; ++x) {
             const int c = (int)tab[x];
@@ -315,12 +306,7 @@ __device__ __forceinline__ void plan_fill(const int16_t* __restrict__ ranked, co
       // each lane owns one word; nwords <= 64 for nb <= 2048
       const uint32_t word = (qt < nwords) ? bits[qr][qt] : 0u;
       const int cnt = __popc(word);
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (qt >= off) incl += y;
-      }
+      const int incl = (int)wave_incl_scan((uint32_t)cnt, qt);
       int pos = incl - cnt;
       uint32_t w = word;
       while (w) {
