@@ -672,12 +672,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     }
     return;
   }
-  __shared__ int wg_sum;
+  __shared__ int wave_sum[4];
   const int first = blockIdx.x * 4 * SEL_ROWS;
   const int last = min(rows, first + 4 * SEL_ROWS) - 1;
   const bool one_head = first / nb == last / nb;  // the common case: pool the workgroup's sum
-  if (threadIdx.x == 0) wg_sum = 0;
-  __syncthreads();
   int head = -1, sum = 0;
   for (int j = 0; j < SEL_ROWS; ++j) {
     const int row = first + wave * SEL_ROWS + j;
@@ -692,12 +690,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     }
     sum += ki;
   }
-  if (head >= 0 && lane == 0) {
-    if (one_head) atomicAdd(&wg_sum, sum);
-    else atomicAdd(&head_count[head], sum);
+  // every wave leaves its sum in its own LDS word (0 without rows), so the
+  // words need no clearing and the workgroup one barrier
+  if (lane == 0) {
+    if (one_head) wave_sum[wave] = head >= 0 ? sum : 0;
+    else if (head >= 0) atomicAdd(&head_count[head], sum);
   }
   __syncthreads();
-  if (threadIdx.x == 0 && one_head) atomicAdd(&head_count[first / nb], wg_sum);
+  if (threadIdx.x == 0 && one_head)
+    atomicAdd(&head_count[first / nb], (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]));
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
