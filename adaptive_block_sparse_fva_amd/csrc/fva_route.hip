@@ -50,7 +50,9 @@ __device__ __forceinline__ void vt_transpose_block(const bf16_t* __restrict__ x,
   constexpr int PER_SB = (VT_KEYS / 8) * DCH;
   for (int w = tid; w < (block / VT_KEYS) * PER_SB; w += 256) {
     const int sb = w / PER_SB, rem = w % PER_SB;
-    const int jc = rem / DCH, dc = rem % DCH;
+    // output chunk fastest: the eight lanes of one feature chunk dc write a
+    // whole 128-byte V^T row (64 keys) in one store instruction
+    const int jc = rem % (VT_KEYS / 8), dc = rem / (VT_KEYS / 8);
     const int k0 = sb * VT_KEYS + 16 * (jc >> 1) + 4 * (jc & 1);
     u32x4 in[8];
 #pragma unroll
