@@ -116,9 +116,11 @@ __device__ __forceinline__ int64_t wave_placement() {
 // sub-block (a kept key block of BLK keys is processed as BLK/KB sub-blocks,
 // numbered u = 0 .. nsub-1 along the tile's kept list).  K and V^T sub-tiles
 // stream through a ring of NBUF LDS slots: sub-block u+NBUF-1 is issued while
-// u is computed.
+// u is computed.  Two waves per SIMD; the B = 64, d = 128 shape, whose
+// 74 KB of LDS allows one wave per SIMD anyway, asks for one.
 template <int D, int BLK, int KB, int NBUF, bool TRACE>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 64 && D == 128 ? 1 : 2,
+                                                                          BLK == 64 && D == 128 ? 1 : 2)))
 void sparse_attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = BLK / 32;   // waves per workgroup (32 query rows each)
   constexpr int SUB = BLK / KB;  // sub-blocks per kept key block
