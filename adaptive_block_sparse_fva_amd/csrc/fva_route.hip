@@ -282,7 +282,6 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-
 // ---------------------------------------------------------------------------
 // 3. Ranking and cutoff.  One wave per (query block i, head h) row at a time,
 // SEL_ROWS consecutive rows per wave and four waves per workgroup; the sort
@@ -293,7 +292,9 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
 //     (strides below E between the lane's registers, larger strides between
 //     lanes): score descending, equal scores by lower id;
 //   - weights w_r = rint(exp(s_(r) - s_(0)) * 2^40) in fp64, an exact integer
-//     inclusive scan along the ranking, target T = fl(p * W);
+//     inclusive scan along the ranking (within each lane's registers, then
+//     across lanes by DPP row shifts and the row totals), target
+//     T = fl(p * W);
 //   - k_p = 1 + #{r : prefix_r < ceil(T)}, k_i = max(k_p, min(k_min, nb)).
 // Integer prefix sums make the cutoff independent of summation order.  The
 // per-head sums of k_i are accumulated per wave and per workgroup before one
