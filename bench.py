@@ -399,8 +399,9 @@ def gsrs_trajectory(stream, steps=10, warmup=2, at=(2, 4, 6, 8), ps=(0.95, 0.9, 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "head-migration path is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library covers one "
+              "GPU's share of the heads, and the multi-GPU head migration is a host-side simulation "
+              "(the balance step), not a multi-GPU run.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
