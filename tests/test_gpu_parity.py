@@ -112,6 +112,24 @@ def test_chain_matches_oracle(name, p):
         check_attention(wl, inp, res, tiles, label=f"{len(tiles)} sampled tiles:")
 
 
+# the two rank shares at thresholds and refills their workload entries do not
+# use: a sparse mask (p = 0.5), the refill at 100 per mille, a near-dense mask
+# (p = 0.99); integer outputs in full, attention on sampled tiles
+MORE_P = [("rank480p", 0.5, 0), ("rank480p", 0.8, 100), ("rank480p", 0.99, 0), ("rank720p", 0.8, 0)]
+
+
+@pytest.mark.parametrize("name,p,refill", MORE_P, ids=[f"{n}-p{p}-r{r}" for n, p, r in MORE_P])
+def test_rank_shares_at_other_thresholds(name, p, refill):
+    wl = WORKLOADS[name]
+    say(f"[gpu] chain {name} p={p} refill={refill}")
+    inp = make_inputs(wl)
+    q, k, v = device_inputs(inp)
+    _, res = run_chain(problem_for(wl, p, refill), q, k, v)
+    check_routing_and_plan(wl, inp, res, p, refill)
+    tiles = sample_tiles(res["row_ptr"], wl.num_heads, res["nb"], per_head=SAMPLED_PER_HEAD, seed=11)
+    check_attention(wl, inp, res, tiles, label=f"{len(tiles)} sampled tiles:")
+
+
 @pytest.mark.parametrize("name", ["tiny", "two_head"])
 def test_p_one_is_dense_attention(name):
     wl = WORKLOADS[name]
