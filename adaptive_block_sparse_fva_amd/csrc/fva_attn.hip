@@ -20,7 +20,8 @@
 //     accumulators hold their keys; B = P converted to bf16 straight from
 //     the S^T accumulators, so no register shuffles are needed;
 //   - K and V come re-laid out in the video-aware order by the routing pass
-//     (K row-major per position, V transposed per 64-position sub-block with
+//     or by fva_kv_layout (K row-major per position, V transposed per
+//     64-position sub-block with
 //     its columns in the order the S^T accumulators hold their keys), so the
 //     kernel streams contiguous sub-tiles into a ring of LDS slots with
 //     direct buffer -> LDS loads whose addresses are per-lane constants plus
