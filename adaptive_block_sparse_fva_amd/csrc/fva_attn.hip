@@ -21,12 +21,11 @@
 //     the S^T accumulators, so no register shuffles are needed;
 //   - K and V come re-laid out in the video-aware order by the routing pass
 //     or by fva_kv_layout (K row-major per position, V transposed per
-//     64-position sub-block with
-//     its columns in the order the S^T accumulators hold their keys), so the
-//     kernel streams contiguous sub-tiles into a ring of LDS slots with
-//     direct buffer -> LDS loads whose addresses are per-lane constants plus
-//     one scalar offset, and reads its V^T operands with plain 16-byte LDS
-//     loads.
+//     64-position sub-block with its columns in the order the S^T
+//     accumulators hold their keys), so the kernel streams contiguous
+//     sub-tiles into a ring of LDS slots with direct buffer -> LDS loads
+//     whose addresses are per-lane constants plus one scalar offset, and
+//     reads its V^T operands with plain 16-byte LDS loads.
 #include <type_traits>
 
 #ifndef FVA_KB
