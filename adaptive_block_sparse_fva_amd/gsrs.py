@@ -1,4 +1,4 @@
-"""Multi-step driver for growing sparsity with reduced search.
+"""Multi-step runner for growing sparsity with reduced search.
 
 "Sparse Attention for Video Generation Acceleration via Growing Sparsity and
 Reduced Search", S5.1 and A.5: dense warm-up steps, a first search over every
